@@ -1,0 +1,218 @@
+/*
+ * pa.h -- paged-KV-cache attention on AMD MI355X (gfx950): the C ABI.
+ *
+ * What the library computes (cited by page title and section):
+ *
+ *   Exact attention softmax(q K^T * scale) V for every query row
+ *   ("FlashAttention and PagedAttention: two fixes for two different
+ *   bottlenecks", section "Why attention is expensive"), where the keys and
+ *   values of each sequence are stored in fixed-size blocks of a shared pool
+ *   and found through a per-sequence block table that maps logical blocks to
+ *   physical ones (same page, "PagedAttention - How it works"; "Flash
+ *   Attention vs Paged Attention", "Paged Attention: memory blocking",
+ *   eq. (4)).  The kernels never build the score matrix: they stream K/V
+ *   tiles and keep a running maximum and running sum per row (the online
+ *   softmax of "FlashAttention - How it works"), which reaches the same
+ *   result as the plain definition up to floating-point rounding.
+ *
+ * Conventions shared by every entry point:
+ *
+ *   - Every tensor is described by a pa_tensor: a device pointer, a dtype,
+ *     a rank and per-dimension sizes and strides (strides in elements).
+ *     The caller owns all memory; the library keeps no pointer after a call
+ *     returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL means the
+ *     default stream).  PA_OK means "validated and launched"; faults caused
+ *     by bad device-side contents (see each call's contract) surface at the
+ *     caller's next synchronisation, not as a status.
+ *   - Every argument that can be checked on the host is checked before any
+ *     GPU work is issued; on failure nothing is launched, a negative
+ *     pa_status is returned and pa_last_error() describes the problem.
+ *   - Layouts (names follow the pages' domain; S sequences, H query heads,
+ *     Hkv KV heads, G = H / Hkv, d head size, B block size, NB pool blocks,
+ *     MB table width, T packed query rows):
+ *       k_pool, v_pool   [NB, B, Hkv, d]  fully contiguous
+ *       block_table      int32 [S, MB]    last dim contiguous
+ *       context_lens     int32 [S]        contiguous; n_s = keys of sequence s
+ *     Logical token t of sequence s lives in physical block
+ *     block_table[s][t / B], slot t % B.  Query head h reads KV head h / G.
+ *   - Supported instances: dtype f32, f16 or bf16 (prefill: f16, bf16);
+ *     d in {64, 128} (prefill: 128); B in {16, 32, 64, 128}; G in {1, 2, 4}.
+ *     Other shapes return PA_ERR_UNSUPPORTED.
+ *   - Device-side contents the host cannot check without a synchronisation
+ *     are the caller's contract: 0 <= n_s <= MB * B; block_table[s][j] in
+ *     [0, NB) for j < ceil(n_s / B).  Entries at j >= ceil(n_s / B) and pool
+ *     slots at or past n_s are never used (they may hold anything, NaN
+ *     included).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_I32 = 3
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required tensor or data pointer is NULL      */
+  PA_ERR_DTYPE = -2,       /* a dtype is not allowed for that argument       */
+  PA_ERR_SHAPE = -3,       /* ranks or sizes are inconsistent                */
+  PA_ERR_STRIDE = -4,      /* a layout/alignment requirement is not met      */
+  PA_ERR_UNSUPPORTED = -5, /* valid, but no compiled instance for it         */
+  PA_ERR_ALLOC = -6,       /* workspace allocation failed                    */
+  PA_ERR_LAUNCH = -7,      /* the HIP runtime refused a launch or call       */
+  PA_ERR_ARG = -8          /* a scalar argument is out of range              */
+} pa_status;
+
+typedef struct pa_tensor {
+  void* data;        /* device pointer (host pointer never accepted)        */
+  int32_t dtype;     /* pa_dtype                                            */
+  int32_t ndim;      /* 1..4                                                */
+  int64_t shape[4];  /* sizes; entries past ndim are ignored                */
+  int64_t stride[4]; /* strides in elements; entries past ndim are ignored  */
+} pa_tensor;
+
+/*
+ * pa_decode -- one query token per sequence attends to its paged KV cache.
+ *
+ * Defines: out[s][h] = sum_t p_t v_t with p = softmax_t(scale * q[s][h] . k_t)
+ * over the n_s logical tokens t of sequence s, k_t / v_t read through the
+ * block table (block-wise form: "Flash Attention vs Paged Attention",
+ * eq. (4); gathering through the table: "How PagedAttention and
+ * RadixAttention optimise KV-cache handling", "How PagedAttention works").
+ *
+ *   q            [S, H, d]   dtype f32/f16/bf16; last dim contiguous;
+ *                            16-byte aligned rows
+ *   k_pool       [NB, B, Hkv, d]  same dtype as q
+ *   v_pool       same shape and dtype as k_pool
+ *   block_table  int32 [S, MB]
+ *   context_lens int32 [S]   n_s >= 0 (n_s = 0 gives a zero output row)
+ *   scale        finite float (1/sqrt(d) for standard attention)
+ *   out          [S, H, d]   dtype f32 or q's dtype; last dim contiguous;
+ *                            must not alias any input
+ *   stream       hipStream_t or NULL
+ *
+ * Long contexts are split into partitions processed in parallel and joined
+ * by a log-sum-exp merge; a workspace of
+ *   S * H * ceil(MB*B / P) * (d + 1) * 4 bytes
+ * (P = partition size chosen from host shapes) is allocated and freed
+ * stream-ordered on `stream` when more than one partition is possible.
+ * Returns PA_OK or a negative pa_status.
+ */
+int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+              const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+              const pa_tensor* out, void* stream);
+
+/*
+ * pa_prefill -- packed query rows of several sequences attend to their paged
+ * KV caches, optionally with a causal mask.
+ *
+ * Sequence s owns packed rows query_start_loc[s] .. query_start_loc[s+1]-1
+ * (L_s rows).  Row i of sequence s sits at absolute position
+ * n_s - L_s + i; with causal != 0 it sees keys t <= n_s - L_s + i
+ * (bottom-right alignment; with L_s = n_s this is the usual lower-
+ * triangular mask of "Flash Attention vs Paged Attention", fused causal
+ * masking), otherwise all n_s keys.  Key tiles wholly above the diagonal
+ * are skipped, never loaded.
+ *
+ *   q                [T, H, d]  f16 or bf16; last dim contiguous
+ *   k_pool, v_pool   [NB, B, Hkv, d]  same dtype as q; the prompt's own
+ *                    K/V must already be in the pool
+ *   block_table      int32 [S, MB]
+ *   context_lens     int32 [S]
+ *   query_start_loc  int32 [S + 1], non-decreasing, query_start_loc[0] = 0,
+ *                    query_start_loc[S] = T (device contents: contract)
+ *   max_query_len    host-side upper bound on every L_s (not checked
+ *                    against the device contents; rows past it are not
+ *                    computed)
+ *   scale            finite float
+ *   causal           0 or 1
+ *   out              [T, H, d]  f32 or q's dtype; must not alias inputs
+ *
+ * Contract: 0 <= L_s <= n_s.  The P.V product runs on fp16 matrix cores
+ * with fp32 accumulation; bf16 V values must lie within the fp16 range
+ * (|v| < 65504).
+ */
+int pa_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+               const pa_tensor* block_table, const pa_tensor* context_lens,
+               const pa_tensor* query_start_loc, int32_t max_query_len, float scale,
+               int32_t causal, const pa_tensor* out, void* stream);
+
+/*
+ * pa_write_kv -- append new tokens' K and V rows to their pool slots.
+ *
+ * Blocks fill left to right and a sequence takes a new block only when its
+ * last one is full ("Flash Attention vs Paged Attention", memory-management
+ * paragraph; "How PagedAttention and RadixAttention optimise KV-cache
+ * handling", "How PagedAttention works", on-demand growth).  The caller's
+ * allocator chooses the slots; this call only moves the bytes.
+ *
+ *   k_new, v_new   [N, Hkv, d]  same dtype as the pools; last dim contiguous
+ *   slot_mapping   int32 [N]; slot x means block x / B, position x % B;
+ *                  x < 0 skips the row.  Slots must be distinct and below
+ *                  NB * B (device contents: contract)
+ *   k_pool, v_pool [NB, B, Hkv, d]  written in place
+ */
+int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
+                const pa_tensor* slot_mapping, const pa_tensor* k_pool,
+                const pa_tensor* v_pool, void* stream);
+
+/* Text for a pa_status value (static storage). */
+const char* pa_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_decode_plan -- what pa_decode would launch for these arguments,
+ * without launching anything (same validation as pa_decode).
+ *
+ *   partition_tokens  keys per partition P
+ *   max_partitions    ceil(MB * B / P)
+ *   grid[3]           workgroups of the partition kernel (x, y, z)
+ *   block_threads     threads per workgroup
+ *   workspace_bytes   stream-ordered workspace (0 if none)
+ *
+ * The environment variable PA_PARTITION_TOKENS (a positive multiple of 64,
+ * at most 4096) overrides P.
+ */
+typedef struct pa_decode_plan_info {
+  int32_t partition_tokens;
+  int32_t max_partitions;
+  int32_t block_threads;
+  int32_t reserved;
+  int64_t grid[3];
+  int64_t workspace_bytes;
+} pa_decode_plan_info;
+
+int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                   const pa_tensor* block_table, const pa_tensor* context_lens,
+                   const pa_tensor* out, pa_decode_plan_info* info);
+
+/*
+ * Kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by a pair of HIP events recorded on the launch stream.
+ * pa_profiler_read synchronises on the recorded events and adds their
+ * elapsed times to per-kernel totals.  Kernel names: "decode_partitions",
+ * "decode_merge", "prefill", "write_kv".  Not meant for concurrent use from
+ * several threads.
+ */
+int pa_profiler_enable(int on);
+void pa_profiler_reset(void);
+/* Returns PA_OK and fills total_ms / launches (0 if the name never ran). */
+int pa_profiler_read(const char* kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -15,8 +15,7 @@ __all__ = ["workloads", "binding", "decode", "prefill", "write_kv"]
 
 def __getattr__(name):
     if name in ("binding", "decode", "prefill", "write_kv"):
-        from . import binding
-        if name == "binding":
-            return binding
-        return getattr(binding, name)
+        import importlib
+        mod = importlib.import_module(__name__ + ".binding")
+        return mod if name == "binding" else getattr(mod, name)
     raise AttributeError(name)

@@ -1,0 +1,175 @@
+"""Python binding of libpa.so: argument marshalling only.
+
+Every function here turns torch tensors into ``pa_tensor`` descriptors
+(device pointer, dtype, shape, strides) and calls the C ABI declared in
+``include/pa.h``; all arithmetic happens in the library's HIP kernels.  torch
+is used for device memory and the current stream, nothing else.  If the
+library is missing or a tensor is not on the GPU the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_F32, PA_F16, PA_BF16, PA_I32 = 0, 1, 2, 3
+_DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+           torch.int32: PA_I32}
+
+PA_OK = 0
+STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_DTYPE", -3: "PA_ERR_SHAPE",
+          -4: "PA_ERR_STRIDE", -5: "PA_ERR_UNSUPPORTED", -6: "PA_ERR_ALLOC",
+          -7: "PA_ERR_LAUNCH", -8: "PA_ERR_ARG"}
+
+
+class PaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class PaDecodePlanInfo(ctypes.Structure):
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("max_partitions", ctypes.c_int32),
+                ("block_threads", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("grid", ctypes.c_int64 * 3), ("workspace_bytes", ctypes.c_int64)]
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+_lib = None
+
+EXPORTS = ("pa_decode", "pa_prefill", "pa_write_kv", "pa_status_string", "pa_last_error",
+           "pa_decode_plan", "pa_profiler_enable", "pa_profiler_reset", "pa_profiler_read")
+
+
+def lib():
+    """Load libpa.so (built in-tree by ``paged_kv_cache_decode_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m paged_kv_cache_decode_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(PaTensor)
+    L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, ctypes.c_void_p]
+    L.pa_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                             P, ctypes.c_void_p]
+    L.pa_write_kv.argtypes = [P, P, P, P, P, ctypes.c_void_p]
+    L.pa_decode_plan.argtypes = [P, P, P, P, P, P, ctypes.POINTER(PaDecodePlanInfo)]
+    for f in ("pa_decode", "pa_prefill", "pa_write_kv", "pa_decode_plan", "pa_profiler_enable",
+              "pa_profiler_read"):
+        getattr(L, f).restype = ctypes.c_int
+    L.pa_status_string.argtypes = [ctypes.c_int]
+    L.pa_status_string.restype = ctypes.c_char_p
+    L.pa_last_error.argtypes = []
+    L.pa_last_error.restype = ctypes.c_char_p
+    L.pa_profiler_enable.argtypes = [ctypes.c_int]
+    L.pa_profiler_reset.argtypes = []
+    L.pa_profiler_reset.restype = None
+    L.pa_profiler_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_int64)]
+    _lib = L
+    return L
+
+
+def describe(t: torch.Tensor) -> PaTensor:
+    """pa_tensor descriptor of a GPU tensor (no copy)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libpa must live on the GPU")
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d = PaTensor()
+    d.data = t.data_ptr() if t.numel() else None
+    d.dtype = _DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PAError(status, lib().pa_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def decode(q, k_pool, v_pool, block_table, context_lens, scale, out=None, out_dtype=None,
+           stream=None):
+    """Paged decode attention; returns ``out [S, H, d]`` (see ``pa_decode``)."""
+    L = lib()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens)]
+    o = describe(out)
+    _check(L.pa_decode(*[ctypes.byref(a) for a in args], ctypes.c_float(scale),
+                       ctypes.byref(o), _stream(stream)))
+    return out
+
+
+def decode_plan(q, k_pool, v_pool, block_table, context_lens, out):
+    """What pa_decode would launch (partition size, grid, workspace)."""
+    L = lib()
+    info = PaDecodePlanInfo()
+    args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens, out)]
+    _check(L.pa_decode_plan(*[ctypes.byref(a) for a in args], ctypes.byref(info)))
+    return dict(partition_tokens=info.partition_tokens, max_partitions=info.max_partitions,
+                block_threads=info.block_threads, grid=tuple(info.grid),
+                workspace_bytes=info.workspace_bytes)
+
+
+def prefill(q, k_pool, v_pool, block_table, context_lens, query_start_loc, max_query_len,
+            scale, causal=True, out=None, out_dtype=None, stream=None):
+    """Paged prefill attention; returns ``out [T, H, d]`` (see ``pa_prefill``)."""
+    L = lib()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens, query_start_loc)]
+    o = describe(out)
+    _check(L.pa_prefill(*[ctypes.byref(a) for a in args], ctypes.c_int32(int(max_query_len)),
+                        ctypes.c_float(scale), ctypes.c_int32(1 if causal else 0),
+                        ctypes.byref(o), _stream(stream)))
+    return out
+
+
+def write_kv(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
+    """Write new tokens' K/V rows into their pool slots, in place."""
+    L = lib()
+    args = [describe(x) for x in (k_new, v_new, slot_mapping, k_pool, v_pool)]
+    _check(L.pa_write_kv(*[ctypes.byref(a) for a in args], _stream(stream)))
+
+
+def profiler_enable(on: bool = True):
+    lib().pa_profiler_enable(1 if on else 0)
+
+
+def profiler_reset():
+    lib().pa_profiler_reset()
+
+
+def profiler_read(kernel: str):
+    """(total milliseconds, launches) recorded for a kernel name."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().pa_profiler_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,232 @@
+// The C ABI of libpa.so: validation (plan.cpp), stream-ordered workspace,
+// kernel launches and error reporting.  See include/pa.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int set_error(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* s = std::getenv("PA_LOG");
+    return s && *s && *s != '0';
+  }();
+  return on;
+}
+
+// Test hook: PA_TEST_FAIL_ALLOC=1 makes every workspace allocation fail.
+bool forced_alloc_failure() {
+  const char* s = std::getenv("PA_TEST_FAIL_ALLOC");
+  return s && *s && *s != '0';
+}
+
+// ---- kernel timer state ---------------------------------------------------
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+struct PendingTiming {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::vector<PendingTiming> g_pending;
+struct Total {
+  double ms = 0;
+  int64_t launches = 0;
+};
+std::map<std::string, Total> g_totals;
+
+void drain_pending_locked() {
+  for (auto& p : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.stop) == hipSuccess &&
+        hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+      Total& t = g_totals[p.name];
+      t.ms += ms;
+      t.launches += 1;
+    }
+    (void)hipEventDestroy(p.start);
+    (void)hipEventDestroy(p.stop);
+  }
+  g_pending.clear();
+}
+
+}  // namespace
+
+namespace pa {
+
+bool profiler_enabled() { return g_prof_on; }
+
+KernelTimer::KernelTimer(const char* name, hipStream_t stream) : name_(name), stream_(stream) {
+  if (!g_prof_on) return;
+  if (hipEventCreate(&start_) != hipSuccess) {
+    start_ = nullptr;
+    return;
+  }
+  if (hipEventRecord(start_, stream_) != hipSuccess) {
+    (void)hipEventDestroy(start_);
+    start_ = nullptr;
+  }
+}
+
+KernelTimer::~KernelTimer() {
+  if (!start_) return;
+  hipEvent_t stop = nullptr;
+  if (hipEventCreate(&stop) != hipSuccess || hipEventRecord(stop, stream_) != hipSuccess) {
+    if (stop) (void)hipEventDestroy(stop);
+    (void)hipEventDestroy(start_);
+    return;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_pending.push_back({name_, start_, stop});
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: dtype not allowed for this argument";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent ranks or sizes";
+    case PA_ERR_STRIDE: return "PA_ERR_STRIDE: layout or alignment requirement not met";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: no compiled instance for these shapes";
+    case PA_ERR_ALLOC: return "PA_ERR_ALLOC: workspace allocation failed";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime refused a call";
+    case PA_ERR_ARG: return "PA_ERR_ARG: scalar argument out of range";
+    default: return "unknown pa_status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                   const pa_tensor* block_table, const pa_tensor* context_lens,
+                   const pa_tensor* out, pa_decode_plan_info* info) {
+  g_last_error.clear();
+  if (!info) return set_error(PA_ERR_NULL, "info is NULL");
+  pa::DecodePlan plan;
+  const int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, 1.0f, out,
+                                 pa::partition_override_from_env(), &plan, &g_last_error);
+  if (st) return st;
+  info->partition_tokens = plan.P;
+  info->max_partitions = plan.MP;
+  info->block_threads = plan.block_threads;
+  info->reserved = 0;
+  for (int i = 0; i < 3; ++i) info->grid[i] = plan.grid[i];
+  info->workspace_bytes = plan.ws_bytes;
+  return PA_OK;
+}
+
+int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+              const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+              const pa_tensor* out, void* stream_ptr) {
+  g_last_error.clear();
+  pa::DecodePlan plan;
+  const int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out,
+                                 pa::partition_override_from_env(), &plan, &g_last_error);
+  if (st) return st;
+  if (plan.S == 0) return PA_OK;
+  if (log_enabled())
+    fprintf(stderr,
+            "[pa] decode dtype=%d out=%d S=%d H=%d Hkv=%d d=%d B=%d MB=%d P=%d MP=%d "
+            "grid=(%lld,%lld,%lld) ws=%lld\n",
+            plan.dtype, plan.out_dtype, plan.S, plan.H, plan.Hkv, plan.D, plan.B, plan.MB,
+            plan.P, plan.MP, (long long)plan.grid[0], (long long)plan.grid[1],
+            (long long)plan.grid[2], (long long)plan.ws_bytes);
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    if (forced_alloc_failure())
+      return set_error(PA_ERR_ALLOC, "workspace of %lld bytes: allocation failure forced by "
+                       "PA_TEST_FAIL_ALLOC", (long long)plan.ws_bytes);
+    const hipError_t e = hipMallocAsync(&ws, (size_t)plan.ws_bytes, stream);
+    if (e != hipSuccess)
+      return set_error(PA_ERR_ALLOC, "hipMallocAsync(%lld bytes): %s", (long long)plan.ws_bytes,
+                       hipGetErrorString(e));
+  }
+  const hipError_t e = pa::launch_decode(plan, ws, stream);
+  if (ws) (void)hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+               const pa_tensor* block_table, const pa_tensor* context_lens,
+               const pa_tensor* query_start_loc, int32_t max_query_len, float scale,
+               int32_t causal, const pa_tensor* out, void* stream_ptr) {
+  g_last_error.clear();
+  pa::PrefillPlan plan;
+  const int st = pa::plan_prefill(q, k_pool, v_pool, block_table, context_lens, query_start_loc,
+                                  max_query_len, scale, causal, out, &plan, &g_last_error);
+  if (st) return st;
+  if (plan.S == 0 || plan.T == 0 || plan.max_query_len == 0) return PA_OK;
+  if (log_enabled())
+    fprintf(stderr, "[pa] prefill dtype=%d S=%d T=%d H=%d Hkv=%d B=%d max_q=%d causal=%d "
+            "workgroups=%lld\n", plan.dtype, plan.S, plan.T, plan.H, plan.Hkv, plan.B,
+            plan.max_query_len, plan.causal, (long long)plan.grid[0]);
+  const hipError_t e = pa::launch_prefill(plan, static_cast<hipStream_t>(stream_ptr));
+  if (e != hipSuccess)
+    return set_error(PA_ERR_LAUNCH, "prefill launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor* slot_mapping,
+                const pa_tensor* k_pool, const pa_tensor* v_pool, void* stream_ptr) {
+  g_last_error.clear();
+  pa::WriteKvPlan plan;
+  const int st = pa::plan_write_kv(k_new, v_new, slot_mapping, k_pool, v_pool, &plan,
+                                   &g_last_error);
+  if (st) return st;
+  const hipError_t e = pa::launch_write_kv(plan, static_cast<hipStream_t>(stream_ptr));
+  if (e != hipSuccess)
+    return set_error(PA_ERR_LAUNCH, "write_kv launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_profiler_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return PA_OK;
+}
+
+void pa_profiler_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending_locked();
+  g_totals.clear();
+}
+
+int pa_profiler_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return set_error(PA_ERR_NULL, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending_locked();
+  auto it = g_totals.find(kernel);
+  *total_ms = it == g_totals.end() ? 0.0 : it->second.ms;
+  *launches = it == g_totals.end() ? 0 : it->second.launches;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,376 @@
+// Host-side validation and launch planning (pure C++, no HIP).
+#include "plan.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+namespace pa {
+namespace {
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    case PA_I32: return 4;
+    default: return 0;
+  }
+}
+
+const char* dtype_name(int dtype) {
+  switch (dtype) {
+    case PA_F32: return "f32";
+    case PA_F16: return "f16";
+    case PA_BF16: return "bf16";
+    case PA_I32: return "i32";
+    default: return "?";
+  }
+}
+
+int fail(std::string* err, int status, const char* fmt, ...)
+    __attribute__((format(printf, 3, 4)));
+
+int fail(std::string* err, int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (err) *err = buf;
+  return status;
+}
+
+// Checks pointer, rank, non-negative sizes and the dtype set.
+int check_basic(const pa_tensor* t, const char* name, int ndim, std::string* err,
+                bool allow_empty_data) {
+  if (!t) return fail(err, PA_ERR_NULL, "%s: tensor descriptor is NULL", name);
+  if (t->ndim != ndim)
+    return fail(err, PA_ERR_SHAPE, "%s: expected %d dimensions, got %d", name, ndim, t->ndim);
+  int64_t numel = 1;
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0)
+      return fail(err, PA_ERR_SHAPE, "%s: negative size %lld in dim %d", name,
+                  (long long)t->shape[i], i);
+    numel *= t->shape[i];
+  }
+  if (!t->data && !(allow_empty_data && numel == 0))
+    return fail(err, PA_ERR_NULL, "%s: data pointer is NULL", name);
+  if (elem_bytes(t->dtype) == 0)
+    return fail(err, PA_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+  return PA_OK;
+}
+
+bool contiguous(const pa_tensor* t) {
+  int64_t expect = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->stride[i] != expect) return false;
+    expect *= t->shape[i];
+  }
+  return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_float(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+
+bool supported_block(int64_t B) { return B == 16 || B == 32 || B == 64 || B == 128; }
+
+bool supported_group(int64_t G) { return G == 1 || G == 2 || G == 4; }
+
+// Pools: [NB, B, Hkv, d], contiguous, same shape and dtype for K and V.
+int check_pools(const pa_tensor* k, const pa_tensor* v, std::string* err) {
+  int st;
+  if ((st = check_basic(k, "k_pool", 4, err, false))) return st;
+  if ((st = check_basic(v, "v_pool", 4, err, false))) return st;
+  if (k->dtype != v->dtype)
+    return fail(err, PA_ERR_DTYPE, "k_pool is %s but v_pool is %s", dtype_name(k->dtype),
+                dtype_name(v->dtype));
+  for (int i = 0; i < 4; ++i)
+    if (k->shape[i] != v->shape[i])
+      return fail(err, PA_ERR_SHAPE, "k_pool and v_pool shapes differ in dim %d", i);
+  if (!contiguous(k) || !contiguous(v))
+    return fail(err, PA_ERR_STRIDE, "k_pool and v_pool must be fully contiguous");
+  if (!aligned16(k->data) || !aligned16(v->data))
+    return fail(err, PA_ERR_STRIDE, "pool base pointers must be 16-byte aligned");
+  if (k->data == v->data)
+    return fail(err, PA_ERR_ARG, "k_pool and v_pool must not alias");
+  return PA_OK;
+}
+
+int check_i32(const pa_tensor* t, const char* name, int ndim, std::string* err) {
+  int st = check_basic(t, name, ndim, err, true);
+  if (st) return st;
+  if (t->dtype != PA_I32) return fail(err, PA_ERR_DTYPE, "%s must be int32", name);
+  if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1)
+    return fail(err, PA_ERR_STRIDE, "%s: last dimension must be contiguous", name);
+  if (t->data && (reinterpret_cast<uintptr_t>(t->data) & 3u))
+    return fail(err, PA_ERR_STRIDE, "%s: data must be 4-byte aligned", name);
+  return PA_OK;
+}
+
+// A [rows, H, d] activation (q or out) with a contiguous last dim and
+// 16-byte aligned rows.
+int check_rows(const pa_tensor* t, const char* name, std::string* err) {
+  int st = check_basic(t, name, 3, err, true);
+  if (st) return st;
+  if (t->shape[2] > 1 && t->stride[2] != 1)
+    return fail(err, PA_ERR_STRIDE, "%s: last dimension must be contiguous", name);
+  const int64_t e = elem_bytes(t->dtype);
+  if (t->data && t->shape[0] * t->shape[1] > 0) {
+    if (!aligned16(t->data) || ((t->stride[0] * e) & 15) || ((t->stride[1] * e) & 15))
+      return fail(err, PA_ERR_STRIDE, "%s: rows must be 16-byte aligned", name);
+  }
+  return PA_OK;
+}
+
+bool ranges_overlap(const pa_tensor* a, const pa_tensor* b) {
+  if (!a->data || !b->data) return false;
+  auto extent = [](const pa_tensor* t) {
+    int64_t hi = 0;
+    for (int i = 0; i < t->ndim; ++i)
+      if (t->shape[i] > 0) hi += (t->shape[i] - 1) * t->stride[i];
+    return (hi + 1) * (int64_t)elem_bytes(t->dtype);
+  };
+  const char* a0 = static_cast<const char*>(a->data);
+  const char* b0 = static_cast<const char*>(b->data);
+  return a0 < b0 + extent(b) && b0 < a0 + extent(a);
+}
+
+}  // namespace
+
+int partition_override_from_env() {
+  const char* s = std::getenv("PA_PARTITION_TOKENS");
+  if (!s || !*s) return 0;
+  char* end = nullptr;
+  long v = std::strtol(s, &end, 10);
+  if (*end || v <= 0 || v % 64 || v > kMaxPartition) return -1;
+  return static_cast<int>(v);
+}
+
+int choose_partition(int S, int Hkv, int max_context, int override_tokens) {
+  if (override_tokens > 0) return override_tokens;
+  // Aim at roughly 2048 partition workgroups for the longest possible
+  // contexts (8 per CU on a 256-CU part) so that long sequences are split
+  // finely enough to balance, without making partitions so short that the
+  // merge traffic matters.  Partitions are whole multiples of 64 keys (one
+  // 16-key tile per wave per round) between 256 and 4096 keys.
+  const double units = static_cast<double>(S) * Hkv;
+  double want = units > 0 ? static_cast<double>(max_context) * units / 2048.0 : 4096.0;
+  int64_t p = static_cast<int64_t>(std::ceil(want / 64.0)) * 64;
+  if (p < 256) p = 256;
+  if (p > kMaxPartition) p = kMaxPartition;
+  return static_cast<int>(p);
+}
+
+int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+                const pa_tensor* out, int partition_override, DecodePlan* plan,
+                std::string* err) {
+  int st;
+  if ((st = check_rows(q, "q", err))) return st;
+  if ((st = check_pools(k_pool, v_pool, err))) return st;
+  if ((st = check_i32(block_table, "block_table", 2, err))) return st;
+  if ((st = check_i32(context_lens, "context_lens", 1, err))) return st;
+  if ((st = check_rows(out, "out", err))) return st;
+  if (!is_float(q->dtype))
+    return fail(err, PA_ERR_DTYPE, "q must be f32, f16 or bf16, got %s", dtype_name(q->dtype));
+  if (k_pool->dtype != q->dtype)
+    return fail(err, PA_ERR_DTYPE, "pools are %s but q is %s", dtype_name(k_pool->dtype),
+                dtype_name(q->dtype));
+  if (out->dtype != PA_F32 && out->dtype != q->dtype)
+    return fail(err, PA_ERR_DTYPE, "out must be f32 or %s, got %s", dtype_name(q->dtype),
+                dtype_name(out->dtype));
+  const int64_t S = q->shape[0], H = q->shape[1], D = q->shape[2];
+  const int64_t NB = k_pool->shape[0], B = k_pool->shape[1], Hkv = k_pool->shape[2];
+  if (k_pool->shape[3] != D)
+    return fail(err, PA_ERR_SHAPE, "pool head size %lld != q head size %lld",
+                (long long)k_pool->shape[3], (long long)D);
+  if (out->shape[0] != S || out->shape[1] != H || out->shape[2] != D)
+    return fail(err, PA_ERR_SHAPE, "out must be [%lld, %lld, %lld]", (long long)S,
+                (long long)H, (long long)D);
+  if (block_table->shape[0] != S)
+    return fail(err, PA_ERR_SHAPE, "block_table has %lld rows, expected %lld",
+                (long long)block_table->shape[0], (long long)S);
+  if (context_lens->shape[0] != S)
+    return fail(err, PA_ERR_SHAPE, "context_lens has %lld entries, expected %lld",
+                (long long)context_lens->shape[0], (long long)S);
+  if (Hkv <= 0 || H <= 0 || H % Hkv)
+    return fail(err, PA_ERR_SHAPE, "query heads %lld not a multiple of KV heads %lld",
+                (long long)H, (long long)Hkv);
+  if (!std::isfinite(scale)) return fail(err, PA_ERR_ARG, "scale must be finite");
+  if (ranges_overlap(out, q) || ranges_overlap(out, k_pool) || ranges_overlap(out, v_pool))
+    return fail(err, PA_ERR_ARG, "out must not alias q or the pools");
+  const int64_t G = H / Hkv;
+  if (!(D == 64 || D == 128))
+    return fail(err, PA_ERR_UNSUPPORTED, "head size %lld not compiled (64, 128)", (long long)D);
+  if (!supported_block(B))
+    return fail(err, PA_ERR_UNSUPPORTED, "block size %lld not compiled (16/32/64/128)",
+                (long long)B);
+  if (!supported_group(G))
+    return fail(err, PA_ERR_UNSUPPORTED, "group size H/Hkv = %lld not compiled (1/2/4)",
+                (long long)G);
+  const int64_t MB = block_table->shape[1];
+  if (S > 0 && MB < 1) return fail(err, PA_ERR_SHAPE, "block_table has no columns");
+  if (S > 65535 || Hkv > 65535)
+    return fail(err, PA_ERR_UNSUPPORTED, "more than 65535 sequences or KV heads");
+  if (MB * B > (int64_t)1 << 30)
+    return fail(err, PA_ERR_UNSUPPORTED, "table covers more than 2^30 keys");
+  if (partition_override < 0)
+    return fail(err, PA_ERR_ARG,
+                "PA_PARTITION_TOKENS must be a positive multiple of 64 up to %d",
+                kMaxPartition);
+
+  DecodePlan p;
+  p.dtype = q->dtype;
+  p.out_dtype = out->dtype;
+  p.S = (int)S; p.H = (int)H; p.Hkv = (int)Hkv; p.G = (int)G; p.D = (int)D; p.B = (int)B;
+  p.MB = (int)MB;
+  p.NB = NB;
+  const int max_ctx = (int)(MB * B);
+  p.P = choose_partition((int)S, (int)Hkv, max_ctx, partition_override);
+  p.MP = (int)((max_ctx + p.P - 1) / p.P);
+  if (p.MP < 1) p.MP = 1;
+  p.grid[0] = p.MP;
+  p.grid[1] = Hkv;
+  p.grid[2] = S;
+  p.block_threads = 64 * kDecodeWaves;
+  p.ws_bytes = p.MP > 1 ? S * H * (int64_t)p.MP * (D + 1) * 4 : 0;
+  p.q = q->data; p.q_ss = q->stride[0]; p.q_sh = q->stride[1];
+  p.k = k_pool->data; p.v = v_pool->data;
+  p.bt = static_cast<const int32_t*>(block_table->data); p.bt_ss = block_table->stride[0];
+  p.cl = static_cast<const int32_t*>(context_lens->data);
+  p.out = out->data; p.o_ss = out->stride[0]; p.o_sh = out->stride[1];
+  p.scale = scale;
+  *plan = p;
+  return PA_OK;
+}
+
+int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                 const pa_tensor* block_table, const pa_tensor* context_lens,
+                 const pa_tensor* query_start_loc, int32_t max_query_len, float scale,
+                 int32_t causal, const pa_tensor* out, PrefillPlan* plan, std::string* err) {
+  int st;
+  if ((st = check_rows(q, "q", err))) return st;
+  if ((st = check_pools(k_pool, v_pool, err))) return st;
+  if ((st = check_i32(block_table, "block_table", 2, err))) return st;
+  if ((st = check_i32(context_lens, "context_lens", 1, err))) return st;
+  if ((st = check_i32(query_start_loc, "query_start_loc", 1, err))) return st;
+  if ((st = check_rows(out, "out", err))) return st;
+  if (!is_float(q->dtype))
+    return fail(err, PA_ERR_DTYPE, "q must be f16 or bf16, got %s", dtype_name(q->dtype));
+  if (k_pool->dtype != q->dtype)
+    return fail(err, PA_ERR_DTYPE, "pools are %s but q is %s", dtype_name(k_pool->dtype),
+                dtype_name(q->dtype));
+  if (out->dtype != PA_F32 && out->dtype != q->dtype)
+    return fail(err, PA_ERR_DTYPE, "out must be f32 or %s, got %s", dtype_name(q->dtype),
+                dtype_name(out->dtype));
+  const int64_t T = q->shape[0], H = q->shape[1], D = q->shape[2];
+  const int64_t NB = k_pool->shape[0], B = k_pool->shape[1], Hkv = k_pool->shape[2];
+  const int64_t S = context_lens->shape[0];
+  if (k_pool->shape[3] != D)
+    return fail(err, PA_ERR_SHAPE, "pool head size %lld != q head size %lld",
+                (long long)k_pool->shape[3], (long long)D);
+  if (out->shape[0] != T || out->shape[1] != H || out->shape[2] != D)
+    return fail(err, PA_ERR_SHAPE, "out must be [%lld, %lld, %lld]", (long long)T,
+                (long long)H, (long long)D);
+  if (block_table->shape[0] != S)
+    return fail(err, PA_ERR_SHAPE, "block_table has %lld rows, expected %lld",
+                (long long)block_table->shape[0], (long long)S);
+  if (query_start_loc->shape[0] != S + 1)
+    return fail(err, PA_ERR_SHAPE, "query_start_loc must have S + 1 = %lld entries",
+                (long long)(S + 1));
+  if (Hkv <= 0 || H <= 0 || H % Hkv)
+    return fail(err, PA_ERR_SHAPE, "query heads %lld not a multiple of KV heads %lld",
+                (long long)H, (long long)Hkv);
+  if (max_query_len < 0) return fail(err, PA_ERR_ARG, "max_query_len must be >= 0");
+  if (causal != 0 && causal != 1) return fail(err, PA_ERR_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(err, PA_ERR_ARG, "scale must be finite");
+  if (ranges_overlap(out, q) || ranges_overlap(out, k_pool) || ranges_overlap(out, v_pool))
+    return fail(err, PA_ERR_ARG, "out must not alias q or the pools");
+  const int64_t G = H / Hkv;
+  if (q->dtype == PA_F32)
+    return fail(err, PA_ERR_UNSUPPORTED, "prefill runs on 16-bit matrix cores (f16, bf16)");
+  if (D != 128)
+    return fail(err, PA_ERR_UNSUPPORTED, "prefill head size %lld not compiled (128)",
+                (long long)D);
+  if (!supported_block(B))
+    return fail(err, PA_ERR_UNSUPPORTED, "block size %lld not compiled (16/32/64/128)",
+                (long long)B);
+  if (!supported_group(G))
+    return fail(err, PA_ERR_UNSUPPORTED, "group size H/Hkv = %lld not compiled (1/2/4)",
+                (long long)G);
+  const int64_t MB = block_table->shape[1];
+  if (S > 0 && MB < 1) return fail(err, PA_ERR_SHAPE, "block_table has no columns");
+  if (MB * B > (int64_t)1 << 30)
+    return fail(err, PA_ERR_UNSUPPORTED, "table covers more than 2^30 keys");
+  if (T > ((int64_t)1 << 31) - 1) return fail(err, PA_ERR_UNSUPPORTED, "too many query rows");
+
+  PrefillPlan p;
+  p.dtype = q->dtype;
+  p.out_dtype = out->dtype;
+  p.S = (int)S; p.T = (int)T; p.H = (int)H; p.Hkv = (int)Hkv; p.G = (int)G; p.D = (int)D;
+  p.B = (int)B; p.MB = (int)MB; p.NB = NB;
+  p.max_query_len = max_query_len;
+  p.causal = causal;
+  p.q_tiles = (max_query_len + kPrefillRows - 1) / kPrefillRows;
+  p.grid[0] = (int64_t)p.q_tiles * Hkv * S;
+  p.grid[1] = 1;
+  p.grid[2] = 1;
+  p.block_threads = 64 * 2 * (int)G;  // 32 query positions of one head per wave
+  p.q = q->data; p.q_st = q->stride[0]; p.q_sh = q->stride[1];
+  p.k = k_pool->data; p.v = v_pool->data;
+  p.bt = static_cast<const int32_t*>(block_table->data); p.bt_ss = block_table->stride[0];
+  p.cl = static_cast<const int32_t*>(context_lens->data);
+  p.qsl = static_cast<const int32_t*>(query_start_loc->data);
+  p.out = out->data; p.o_st = out->stride[0]; p.o_sh = out->stride[1];
+  p.scale = scale;
+  *plan = p;
+  return PA_OK;
+}
+
+int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
+                  const pa_tensor* slot_mapping, const pa_tensor* k_pool,
+                  const pa_tensor* v_pool, WriteKvPlan* plan, std::string* err) {
+  int st;
+  if ((st = check_rows(k_new, "k_new", err))) return st;
+  if ((st = check_rows(v_new, "v_new", err))) return st;
+  if ((st = check_i32(slot_mapping, "slot_mapping", 1, err))) return st;
+  if ((st = check_pools(k_pool, v_pool, err))) return st;
+  if (k_new->dtype != k_pool->dtype || v_new->dtype != k_pool->dtype)
+    return fail(err, PA_ERR_DTYPE, "new rows and pools must share a dtype");
+  if (!is_float(k_pool->dtype)) return fail(err, PA_ERR_DTYPE, "pools must be f32/f16/bf16");
+  const int64_t N = k_new->shape[0];
+  const int64_t NB = k_pool->shape[0], B = k_pool->shape[1], Hkv = k_pool->shape[2],
+                D = k_pool->shape[3];
+  for (int i = 0; i < 3; ++i)
+    if (k_new->shape[i] != v_new->shape[i])
+      return fail(err, PA_ERR_SHAPE, "k_new and v_new shapes differ");
+  if (k_new->shape[1] != Hkv || k_new->shape[2] != D)
+    return fail(err, PA_ERR_SHAPE, "new rows must be [N, %lld, %lld]", (long long)Hkv,
+                (long long)D);
+  if (slot_mapping->shape[0] != N)
+    return fail(err, PA_ERR_SHAPE, "slot_mapping has %lld entries, expected %lld",
+                (long long)slot_mapping->shape[0], (long long)N);
+  if ((D * elem_bytes(k_pool->dtype)) % 16)
+    return fail(err, PA_ERR_UNSUPPORTED, "rows must be a multiple of 16 bytes");
+  if (N > ((int64_t)1 << 31) - 1 || NB * B > ((int64_t)1 << 31) - 1)
+    return fail(err, PA_ERR_UNSUPPORTED, "slot numbers must fit in int32");
+  if (ranges_overlap(k_new, k_pool) || ranges_overlap(v_new, v_pool) ||
+      ranges_overlap(k_new, v_pool) || ranges_overlap(v_new, k_pool))
+    return fail(err, PA_ERR_ARG, "new rows must not alias the pools");
+  WriteKvPlan p;
+  p.dtype = k_pool->dtype;
+  p.N = N; p.NB = NB; p.B = (int)B; p.Hkv = (int)Hkv; p.D = (int)D;
+  p.kn = k_new->data; p.vn = v_new->data;
+  p.kn_s = k_new->stride[0]; p.kn_h = k_new->stride[1];
+  p.vn_s = v_new->stride[0]; p.vn_h = v_new->stride[1];
+  p.slots = static_cast<const int32_t*>(slot_mapping->data);
+  p.kp = k_pool->data; p.vp = v_pool->data;
+  *plan = p;
+  return PA_OK;
+}
+
+}  // namespace pa

@@ -1,0 +1,102 @@
+// Host-side validation and launch planning for the paged-attention kernels.
+//
+// Pure C++: no HIP headers, no device access.  Every check here uses host
+// shapes only, so a call that fails validation issues no GPU work.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+// Decode partition kernel geometry: each workgroup has kDecodeWaves
+// wavefronts of 64 lanes and processes one partition of P keys for one
+// (sequence, KV head); a wavefront handles 16-key tiles.
+constexpr int kDecodeWaves = 4;
+constexpr int kTileKeys = 16;
+constexpr int kMaxPartition = 64 * kTileKeys * kDecodeWaves;  // 4096 keys
+
+struct DecodePlan {
+  int dtype = 0;      // pa_dtype of q / pools
+  int out_dtype = 0;  // PA_F32 or dtype
+  int S = 0, H = 0, Hkv = 0, G = 0, D = 0, B = 0, MB = 0;
+  int64_t NB = 0;
+  int P = 0;   // keys per partition
+  int MP = 0;  // max partitions per sequence
+  int64_t grid[3] = {0, 0, 0};
+  int block_threads = 0;
+  int64_t ws_bytes = 0;  // partial outputs + log-sum-exp, 0 when MP == 1
+  // operands
+  const void* q = nullptr;
+  int64_t q_ss = 0, q_sh = 0;  // strides (elements) over sequence and head
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* bt = nullptr;
+  int64_t bt_ss = 0;
+  const int32_t* cl = nullptr;
+  void* out = nullptr;
+  int64_t o_ss = 0, o_sh = 0;
+  float scale = 0.f;
+};
+
+struct PrefillPlan {
+  int dtype = 0, out_dtype = 0;
+  int S = 0, T = 0, H = 0, Hkv = 0, G = 0, D = 0, B = 0, MB = 0;
+  int64_t NB = 0;
+  int max_query_len = 0;
+  int causal = 0;
+  int q_tiles = 0;  // ceil(max_query_len / kPrefillRows)
+  int64_t grid[3] = {0, 0, 0};
+  int block_threads = 0;
+  const void* q = nullptr;
+  int64_t q_st = 0, q_sh = 0;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* bt = nullptr;
+  int64_t bt_ss = 0;
+  const int32_t* cl = nullptr;
+  const int32_t* qsl = nullptr;
+  void* out = nullptr;
+  int64_t o_st = 0, o_sh = 0;
+  float scale = 0.f;
+};
+
+// Query positions per prefill workgroup (all G heads of one KV head).
+constexpr int kPrefillRows = 64;
+
+struct WriteKvPlan {
+  int dtype = 0;
+  int64_t N = 0, NB = 0;
+  int B = 0, Hkv = 0, D = 0;
+  const void* kn = nullptr;
+  const void* vn = nullptr;
+  int64_t kn_s = 0, kn_h = 0, vn_s = 0, vn_h = 0;
+  const int32_t* slots = nullptr;
+  void* kp = nullptr;
+  void* vp = nullptr;
+};
+
+// Partition size for decode from host shapes (and PA_PARTITION_TOKENS).
+int choose_partition(int S, int Hkv, int max_context, int override_tokens);
+
+int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+                const pa_tensor* out, int partition_override, DecodePlan* plan,
+                std::string* err);
+
+int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                 const pa_tensor* block_table, const pa_tensor* context_lens,
+                 const pa_tensor* query_start_loc, int32_t max_query_len, float scale,
+                 int32_t causal, const pa_tensor* out, PrefillPlan* plan, std::string* err);
+
+int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
+                  const pa_tensor* slot_mapping, const pa_tensor* k_pool,
+                  const pa_tensor* v_pool, WriteKvPlan* plan, std::string* err);
+
+// Reads PA_PARTITION_TOKENS; 0 when unset.  Returns -1 when set but invalid.
+int partition_override_from_env();
+
+}  // namespace pa

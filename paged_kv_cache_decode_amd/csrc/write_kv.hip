@@ -1,0 +1,67 @@
+// Append new tokens' K/V rows into their pool slots (gfx950).
+//
+// The pool fills block by block, left to right; the caller's allocator
+// picks each new token's slot ("Flash Attention vs Paged Attention",
+// memory-management paragraph: blocks fill left to right, unfilled slots
+// are reserved).  This kernel only moves bytes: one thread copies one
+// 16-byte piece of a K row and the same piece of the V row.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pa {
+namespace {
+
+struct WriteKvArgs {
+  const uint8_t* kn;
+  const uint8_t* vn;
+  int64_t kn_s, kn_h, vn_s, vn_h;  // bytes
+  const int32_t* slots;
+  uint8_t* kp;
+  uint8_t* vp;
+  int64_t N;
+  int Hkv, row_bytes, chunks;  // chunks = row_bytes / 16
+};
+
+__global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_tok = (int64_t)a.Hkv * a.chunks;
+  if (idx >= a.N * per_tok) return;
+  const int64_t i = idx / per_tok;
+  const int rem = (int)(idx % per_tok);
+  const int h = rem / a.chunks, ch = rem % a.chunks;
+  const int32_t slot = a.slots[i];
+  if (slot < 0) return;
+  // Slot x is block x / B, position x % B; with the pool contiguous that is
+  // simply row x of the [NB * B, Hkv, d] view.
+  const int64_t dst = ((int64_t)slot * a.Hkv + h) * a.row_bytes + ch * 16;
+  *reinterpret_cast<u32x4_t*>(a.kp + dst) = load16(a.kn + i * a.kn_s + h * a.kn_h + ch * 16);
+  *reinterpret_cast<u32x4_t*>(a.vp + dst) = load16(a.vn + i * a.vn_s + h * a.vn_h + ch * 16);
+}
+
+}  // namespace
+
+hipError_t launch_write_kv(const WriteKvPlan& pl, hipStream_t stream) {
+  const int e = pl.dtype == PA_F32 ? 4 : 2;
+  WriteKvArgs a;
+  a.kn = static_cast<const uint8_t*>(pl.kn);
+  a.vn = static_cast<const uint8_t*>(pl.vn);
+  a.kn_s = pl.kn_s * e;
+  a.kn_h = pl.kn_h * e;
+  a.vn_s = pl.vn_s * e;
+  a.vn_h = pl.vn_h * e;
+  a.slots = pl.slots;
+  a.kp = static_cast<uint8_t*>(pl.kp);
+  a.vp = static_cast<uint8_t*>(pl.vp);
+  a.N = pl.N;
+  a.Hkv = pl.Hkv;
+  a.row_bytes = pl.D * e;
+  a.chunks = a.row_bytes / 16;
+  const int64_t total = pl.N * pl.Hkv * a.chunks;
+  if (total == 0) return hipSuccess;
+  KernelTimer t("write_kv", stream);
+  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa
