@@ -1,0 +1,308 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
+
+Headline (the JSON line's ``value``): ``pa_decode`` on the batched GQA
+decode workload -- 64 sequences, 32 query / 8 KV heads, d = 128, context
+lengths uniform in [128, 4096], block size 16, fp16 -- as achieved HBM GB/s
+of algorithmic bytes (every attended K/V row once per KV head, q, out, the
+table entries used) per step.  One step = one ``pa_decode`` call (partition
+kernel + merge).  Inputs are resident in HBM; steps rotate over three copies
+of the pools so that the 256 MB Infinity Cache cannot hold the 0.55 GB of
+K/V between steps.
+
+The same line carries:
+* ``roofline``: the partition kernel's algorithmic bytes / its average
+  duration, from HIP events the library records around each launch on the
+  launch stream, over a second pass of the same K steps; ``traffic`` comes
+  from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when that
+  summary was taken on the current kernel source, else null.
+* ``cpu_baseline``: the fp64 CPU oracle on the same workload.
+* ``extra``: the long-context decode (4 x 100,000 keys, bf16), the
+  prefix-shared decode sweep (B = 16/32/64/128) and the causal prefill
+  (8 prompts of 512..4096 tokens, bf16; TFLOP/s against the bf16 MFMA peak).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the extra workloads and the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="comma list of workloads to run (for profiling): "
+                         "gqa,long,prefix,prefill")
+    return ap.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_decode_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, src_hash, bytes_per_launch):
+    """HBM traffic measured by rocprofv3 counters, if taken on this source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
+            "ratio_to_algorithmic": round((rec["fetch_bytes"] + rec["write_bytes"]) /
+                                          bytes_per_launch, 4),
+            "scale_factor": rec.get("scale_factor"), "source": os.path.basename(path)}
+
+
+class Timer:
+    """Wall clock over K steps, bracketed by device synchronisation."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps):
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        self.torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+
+def kernel_avg_ms(binding, name):
+    ms, n = binding.profiler_read(name)
+    return (ms / n if n else float("nan")), n
+
+
+def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype):
+    """Time pa_decode on a case, rotating over `copies` device copies of the
+    pools.  Returns a dict of timings."""
+    devs = [binding.upload_case(case) for _ in range(copies)]
+    out = torch.empty(case.q.shape, dtype=out_dtype, device="cuda")
+    calls = [binding.PreparedDecode(d["q"], d["k_pool"], d["v_pool"], d["block_table"],
+                                    d["context_lens"], case.scale, out) for d in devs]
+    plan = binding.decode_plan(devs[0]["q"], devs[0]["k_pool"], devs[0]["v_pool"],
+                               devs[0]["block_table"], devs[0]["context_lens"], out)
+    step = lambda i: calls[i % copies]()  # noqa: E731
+    timer = Timer(torch)
+    for i in range(warmup):
+        step(i)
+    sec = timer.run(step, steps)
+    # Second pass with the library's per-kernel event timer on.
+    binding.profiler_reset()
+    binding.profiler_enable(True)
+    timer.run(step, steps)
+    binding.profiler_enable(False)
+    part_ms, part_n = kernel_avg_ms(binding, "decode_partitions")
+    merge_ms, merge_n = kernel_avg_ms(binding, "decode_merge")
+    binding.profiler_reset()
+    del calls, devs
+    torch.cuda.empty_cache()
+    return dict(sec=sec, part_ms=part_ms, part_launches=part_n,
+                merge_ms=merge_ms if merge_n else 0.0, plan=plan)
+
+
+def cpu_oracle_decode(case, budget_s=20.0):
+    """The fp64 oracle on the workload, timed on the host."""
+    import oracle
+    t0 = time.perf_counter()
+    c0 = time.process_time()
+    passes = 0
+    while True:
+        oracle.decode(case.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
+                      case.scale, case.dtype)
+        passes += 1
+        if time.perf_counter() - t0 > budget_s / 2 or passes >= 3:
+            break
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return wall / passes, max(1, math.ceil(cpu / wall)), passes
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the decode and "
+              "prefill kernels shard by sequence or KV head with no exchange, and this build "
+              "measures the one-GPU share.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_decode_amd import binding
+    from paged_kv_cache_decode_amd import workloads as W
+
+    binding.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    only = set(x for x in a.only.split(",") if x)
+    want = lambda k: not only or k in only  # noqa: E731
+    result = {}
+    extra = {}
+
+    # ---------------- headline: batched GQA decode, fp16 -----------------
+    if want("gqa"):
+        case = W.gqa_f16_decode()
+        nbytes = W.decode_bytes(case, out_bytes_per_elem=2)
+        r = bench_decode_case(torch, binding, case, a.steps, a.warmup, 3, torch.float16)
+        gbs = nbytes / r["sec"] / 1e9
+        part_gbs = nbytes / (r["part_ms"] * 1e-3) / 1e9
+        src = source_hash("decode.hip")
+        roof = {"bound": "hbm", "achieved": round(part_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic("decode_partitions", "gqa-f16-decode", src, nbytes),
+                "kernel": "decode_partitions_kernel<f16,128,4>",
+                "kernel_avg_us": round(r["part_ms"] * 1e3, 2),
+                "merge_avg_us": round(r["merge_ms"] * 1e3, 2),
+                "algorithmic_bytes_per_launch": nbytes}
+        result = {
+            "metric": "Paged attn: decode HBM GB/s (% of peak); causal prefill TFLOP/s "
+                      "(% MFMA peak)",
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": a.steps,
+            "warmup": a.warmup,
+            "ms_per_step": round(r["sec"] * 1e3, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f16",
+            "data": "synthetic",
+            "config": {"workload": "gqa-f16-decode", "seqs": 64, "heads": 32, "kv_heads": 8,
+                       "head_dim": 128, "block_size": 16, "context": "uniform[128,4096]",
+                       "total_keys": int(case.context_lens.sum()), "out": "f16",
+                       "pool_copies_rotated": 3, "partition_tokens":
+                           r["plan"]["partition_tokens"]},
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "roofline": roof,
+        }
+        if not a.headline_only and not a.no_cpu_baseline:
+            sec, cores, passes = cpu_oracle_decode(case)
+            result["cpu_baseline"] = {
+                "value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"the whole workload (64 sequences x 32 heads), {passes} pass(es), "
+                          f"{sec:.2f} s per pass, fp64 numpy"}
+        del case
+
+    if not a.headline_only:
+        # ---------------- long-context decode, bf16 ----------------------
+        if want("long"):
+            case = W.long_bf16_decode()
+            nbytes = W.decode_bytes(case, out_bytes_per_elem=2)
+            r = bench_decode_case(torch, binding, case, max(10, a.steps // 2), 3, 1,
+                                  torch.bfloat16)
+            extra["long-bf16-decode"] = {
+                "GB/s": round(nbytes / r["sec"] / 1e9, 1),
+                "frac_of_hbm_peak": round(nbytes / r["sec"] / 1e9 / HBM_PEAK_GBS, 4),
+                "ms_per_step": round(r["sec"] * 1e3, 4),
+                "partition_kernel_GB/s": round(nbytes / (r["part_ms"] * 1e-3) / 1e9, 1),
+                "partition_kernel_avg_us": round(r["part_ms"] * 1e3, 2),
+                "merge_avg_us": round(r["merge_ms"] * 1e3, 2),
+                "partition_tokens": r["plan"]["partition_tokens"],
+                "algorithmic_bytes": nbytes}
+            del case
+        # ---------------- prefix-shared decode sweep ---------------------
+        if want("prefix"):
+            for B in (16, 32, 64, 128):
+                case = W.prefix_shared_bf16_decode(B)
+                logical = W.decode_bytes(case, out_bytes_per_elem=2)
+                unique = (case.meta["unique_tokens"] * 8 * 128 * 2 * 2 +
+                          logical - int(case.context_lens.sum()) * 8 * 128 * 2 * 2)
+                r = bench_decode_case(torch, binding, case, max(10, a.steps // 2), 3, 3,
+                                      torch.bfloat16)
+                extra[f"prefix-shared-bf16-decode-B{B}"] = {
+                    "unique_GB/s": round(unique / r["sec"] / 1e9, 1),
+                    "frac_of_hbm_peak_unique": round(unique / r["sec"] / 1e9 / HBM_PEAK_GBS, 4),
+                    "logical_GB/s": round(logical / r["sec"] / 1e9, 1),
+                    "ms_per_step": round(r["sec"] * 1e3, 4),
+                    "partition_kernel_avg_us": round(r["part_ms"] * 1e3, 2),
+                    "unique_bytes": unique, "logical_bytes": logical}
+                del case
+        # ---------------- causal prefill, bf16 ---------------------------
+        if want("prefill"):
+            case = W.causal_bf16_prefill()
+            flops = W.prefill_flops(case)
+            d = binding.upload_case(case)
+            out = torch.empty(case.q.shape, dtype=torch.bfloat16, device="cuda")
+            call = binding.PreparedPrefill(d["q"], d["k_pool"], d["v_pool"], d["block_table"],
+                                           d["context_lens"], d["query_start_loc"],
+                                           case.max_query_len, case.scale, True, out)
+            timer = Timer(torch)
+            for _ in range(3):
+                call()
+            steps = max(10, a.steps // 2)
+            sec = timer.run(lambda i: call(), steps)
+            binding.profiler_reset()
+            binding.profiler_enable(True)
+            timer.run(lambda i: call(), steps)
+            binding.profiler_enable(False)
+            k_ms, _ = kernel_avg_ms(binding, "prefill")
+            binding.profiler_reset()
+            tf = flops / sec / 1e12
+            ktf = flops / (k_ms * 1e-3) / 1e12
+            entry = {"TFLOP/s": round(tf, 1), "frac_of_bf16_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "ms_per_step": round(sec * 1e3, 4), "flops": flops,
+                     "prompt_lens": case.meta["lens"],
+                     "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
+                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(ktf / BF16_PEAK_TFLOPS, 4),
+                                  "kernel": "prefill_kernel<bf16,4>",
+                                  "kernel_avg_us": round(k_ms * 1e3, 2)}}
+            if not a.no_cpu_baseline:
+                import oracle
+                s0 = 1  # one prompt of the eight (515 tokens), all 32 heads
+                qsl = case.query_start_loc
+                sub_q = case.q[qsl[s0]:qsl[s0 + 1]]
+                t0 = time.perf_counter()
+                c0 = time.process_time()
+                oracle.prefill(sub_q, case.k_pool, case.v_pool, case.block_table[s0:s0 + 1],
+                               case.context_lens[s0:s0 + 1],
+                               np.array([0, qsl[s0 + 1] - qsl[s0]], dtype=np.int32),
+                               case.scale, True, case.dtype)
+                wall = time.perf_counter() - t0
+                cpu = time.process_time() - c0
+                L = int(qsl[s0 + 1] - qsl[s0])
+                sub_flops = 2 * 32 * 128 * L * (L + 1)
+                entry["cpu_baseline"] = {
+                    "value": round(sub_flops / wall / 1e12, 6), "unit": "TFLOP/s",
+                    "cores": max(1, math.ceil(cpu / wall)), "kind": "oracle",
+                    "sample": f"prompt {s0} ({L} tokens), all 32 heads, fp64 numpy, "
+                              f"{wall:.2f} s"}
+            extra["causal-bf16-prefill"] = entry
+            del d, call
+    if extra:
+        result["extra"] = extra
+    if not result:
+        result = {"extra": extra}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -173,3 +173,64 @@ def profiler_read(kernel: str):
     n = ctypes.c_int64()
     _check(lib().pa_profiler_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+class PreparedDecode:
+    """A pa_decode call with its descriptors built once (for tight loops)."""
+
+    def __init__(self, q, k_pool, v_pool, block_table, context_lens, scale, out):
+        self._keep = (q, k_pool, v_pool, block_table, context_lens, out)
+        self._args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens)]
+        self._out = describe(out)
+        self._refs = [ctypes.byref(x) for x in self._args]
+        self._scale = ctypes.c_float(scale)
+        self._L = lib()
+
+    def __call__(self, stream=None):
+        _check(self._L.pa_decode(*self._refs, self._scale, ctypes.byref(self._out),
+                                 _stream(stream)))
+        return self._keep[-1]
+
+
+class PreparedPrefill:
+    """A pa_prefill call with its descriptors built once."""
+
+    def __init__(self, q, k_pool, v_pool, block_table, context_lens, query_start_loc,
+                 max_query_len, scale, causal, out):
+        self._keep = (q, k_pool, v_pool, block_table, context_lens, query_start_loc, out)
+        self._args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens,
+                                            query_start_loc)]
+        self._out = describe(out)
+        self._refs = [ctypes.byref(x) for x in self._args]
+        self._maxq = ctypes.c_int32(int(max_query_len))
+        self._scale = ctypes.c_float(scale)
+        self._causal = ctypes.c_int32(1 if causal else 0)
+        self._L = lib()
+
+    def __call__(self, stream=None):
+        _check(self._L.pa_prefill(*self._refs, self._maxq, self._scale, self._causal,
+                                  ctypes.byref(self._out), _stream(stream)))
+        return self._keep[-1]
+
+
+_TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def upload(a, dtype: str | None = None) -> torch.Tensor:
+    """Copy a storage-format numpy array (uint16 bit patterns for 16-bit
+    formats) to a GPU tensor of the matching torch dtype."""
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(_TORCH_DT[dtype]).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def upload_case(case) -> dict:
+    """Device copies of a workloads.PagedCase's arrays."""
+    d = dict(q=upload(case.q, case.dtype), k_pool=upload(case.k_pool, case.dtype),
+             v_pool=upload(case.v_pool, case.dtype), block_table=upload(case.block_table),
+             context_lens=upload(case.context_lens))
+    if case.query_start_loc is not None:
+        d["query_start_loc"] = upload(case.query_start_loc)
+    return d
