@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the extra workloads and the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch) 10 times, to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--only", default="",
                     help="comma list of workloads to run (for profiling): "
                          "gqa,long,prefix,prefill")
@@ -160,6 +163,14 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 10}))
+        return
     only = set(x for x in a.only.split(",") if x)
     want = lambda k: not only or k in only  # noqa: E731
     result = {}
@@ -197,8 +208,7 @@ def main():
             "config": {"workload": "gqa-f16-decode", "seqs": 64, "heads": 32, "kv_heads": 8,
                        "head_dim": 128, "block_size": 16, "context": "uniform[128,4096]",
                        "total_keys": int(case.context_lens.sum()), "out": "f16",
-                       "pool_copies_rotated": 3, "partition_tokens":
-                           r["plan"]["partition_tokens"]},
+                       "pool_copies_rotated": 3, "decode_workers": r["plan"]["workers"]},
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "roofline": roof,
         }
@@ -225,7 +235,7 @@ def main():
                 "partition_kernel_GB/s": round(nbytes / (r["part_ms"] * 1e-3) / 1e9, 1),
                 "partition_kernel_avg_us": round(r["part_ms"] * 1e3, 2),
                 "merge_avg_us": round(r["merge_ms"] * 1e3, 2),
-                "partition_tokens": r["plan"]["partition_tokens"],
+                "decode_workers": r["plan"]["workers"],
                 "algorithmic_bytes": nbytes}
             del case
         # ---------------- prefix-shared decode sweep ---------------------

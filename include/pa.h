@@ -101,11 +101,13 @@ typedef struct pa_tensor {
  *                            must not alias any input
  *   stream       hipStream_t or NULL
  *
- * Long contexts are split into partitions processed in parallel and joined
- * by a log-sum-exp merge; a workspace of
- *   S * H * ceil(MB*B / P) * (d + 1) * 4 bytes
- * (P = partition size chosen from host shapes) is allocated and freed
- * stream-ordered on `stream` when more than one partition is possible.
+ * Work is balanced over a fixed set of W wavefronts (the device's resident
+ * capacity): the 16-key tiles of all (sequence, KV head) pairs form one list
+ * that is cut into W equal contiguous slices, so long contexts are split
+ * into partitions processed in parallel and joined by a log-sum-exp merge.
+ * A workspace of
+ *   (W + S*Hkv) * G * (d + 1) * 4 + S * Hkv * 8 bytes
+ * is allocated and freed stream-ordered on `stream` (hipMallocAsync).
  * Returns PA_OK or a negative pa_status.
  */
 int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
@@ -176,18 +178,18 @@ const char* pa_last_error(void);
  * pa_decode_plan -- what pa_decode would launch for these arguments,
  * without launching anything (same validation as pa_decode).
  *
- *   partition_tokens  keys per partition P
- *   max_partitions    ceil(MB * B / P)
- *   grid[3]           workgroups of the partition kernel (x, y, z)
+ *   workers           wavefronts W sharing the tile list
+ *   waves_per_group   wavefronts per workgroup
+ *   grid[3]           workgroups of the partition kernel
  *   block_threads     threads per workgroup
- *   workspace_bytes   stream-ordered workspace (0 if none)
+ *   workspace_bytes   stream-ordered workspace
  *
- * The environment variable PA_PARTITION_TOKENS (a positive multiple of 64,
- * at most 4096) overrides P.
+ * The environment variable PA_DECODE_WORKERS (1 .. 2^20) overrides W; the
+ * result is the same up to floating-point rounding for every W.
  */
 typedef struct pa_decode_plan_info {
-  int32_t partition_tokens;
-  int32_t max_partitions;
+  int32_t workers;
+  int32_t waves_per_group;
   int32_t block_threads;
   int32_t reserved;
   int64_t grid[3];

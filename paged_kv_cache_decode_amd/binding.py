@@ -15,7 +15,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libpa.so")
+# PA_LIBRARY may point at another build of the same library (A/B timing).
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_PKG, "libpa.so")
 
 PA_F32, PA_F16, PA_BF16, PA_I32 = 0, 1, 2, 3
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
@@ -33,7 +34,7 @@ class PaTensor(ctypes.Structure):
 
 
 class PaDecodePlanInfo(ctypes.Structure):
-    _fields_ = [("partition_tokens", ctypes.c_int32), ("max_partitions", ctypes.c_int32),
+    _fields_ = [("workers", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("grid", ctypes.c_int64 * 3), ("workspace_bytes", ctypes.c_int64)]
 
@@ -128,12 +129,12 @@ def decode(q, k_pool, v_pool, block_table, context_lens, scale, out=None, out_dt
 
 
 def decode_plan(q, k_pool, v_pool, block_table, context_lens, out):
-    """What pa_decode would launch (partition size, grid, workspace)."""
+    """What pa_decode would launch (workers, grid, workspace)."""
     L = lib()
     info = PaDecodePlanInfo()
     args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens, out)]
     _check(L.pa_decode_plan(*[ctypes.byref(a) for a in args], ctypes.byref(info)))
-    return dict(partition_tokens=info.partition_tokens, max_partitions=info.max_partitions,
+    return dict(workers=info.workers, waves_per_group=info.waves_per_group,
                 block_threads=info.block_threads, grid=tuple(info.grid),
                 workspace_bytes=info.workspace_bytes)
 

@@ -123,17 +123,35 @@ const char* pa_status_string(int status) {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
+namespace {
+
+// Workers for a decode call: PA_DECODE_WORKERS if set, else the device's
+// resident capacity for the instance the shapes select.
+int decode_workers(const pa_tensor* q, const pa_tensor* k_pool) {
+  const int ov = pa::workers_override_from_env();
+  if (ov != 0) return ov;  // -1 (invalid) is rejected by the planner
+  if (!q || !k_pool) return 1;
+  const int64_t H = q->shape[1], Hkv = k_pool->shape[2];
+  const int G = (Hkv > 0 && H % Hkv == 0) ? (int)(H / Hkv) : 1;
+  return pa::decode_worker_count(q->dtype, (int)q->shape[2], G);
+}
+
+}  // namespace
+
 int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
                    const pa_tensor* block_table, const pa_tensor* context_lens,
                    const pa_tensor* out, pa_decode_plan_info* info) {
   g_last_error.clear();
   if (!info) return set_error(PA_ERR_NULL, "info is NULL");
   pa::DecodePlan plan;
-  const int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, 1.0f, out,
-                                 pa::partition_override_from_env(), &plan, &g_last_error);
+  int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, 1.0f, out, 1, &plan,
+                           &g_last_error);
   if (st) return st;
-  info->partition_tokens = plan.P;
-  info->max_partitions = plan.MP;
+  st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, 1.0f, out,
+                       decode_workers(q, k_pool), &plan, &g_last_error);
+  if (st) return st;
+  info->workers = plan.workers;
+  info->waves_per_group = pa::kDecodeWaves;
   info->block_threads = plan.block_threads;
   info->reserved = 0;
   for (int i = 0; i < 3; ++i) info->grid[i] = plan.grid[i];
@@ -146,20 +164,23 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_po
               const pa_tensor* out, void* stream_ptr) {
   g_last_error.clear();
   pa::DecodePlan plan;
-  const int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out,
-                                 pa::partition_override_from_env(), &plan, &g_last_error);
+  // Validate first (no device query for invalid arguments), then size.
+  int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out, 1, &plan,
+                           &g_last_error);
   if (st) return st;
   if (plan.S == 0) return PA_OK;
+  st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out,
+                       decode_workers(q, k_pool), &plan, &g_last_error);
+  if (st) return st;
   if (log_enabled())
     fprintf(stderr,
-            "[pa] decode dtype=%d out=%d S=%d H=%d Hkv=%d d=%d B=%d MB=%d P=%d MP=%d "
-            "grid=(%lld,%lld,%lld) ws=%lld\n",
+            "[pa] decode dtype=%d out=%d S=%d H=%d Hkv=%d d=%d B=%d MB=%d workers=%d "
+            "groups=%lld ws=%lld\n",
             plan.dtype, plan.out_dtype, plan.S, plan.H, plan.Hkv, plan.D, plan.B, plan.MB,
-            plan.P, plan.MP, (long long)plan.grid[0], (long long)plan.grid[1],
-            (long long)plan.grid[2], (long long)plan.ws_bytes);
+            plan.workers, (long long)plan.grid[0], (long long)plan.ws_bytes);
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   void* ws = nullptr;
-  if (plan.ws_bytes > 0) {
+  {
     if (forced_alloc_failure())
       return set_error(PA_ERR_ALLOC, "workspace of %lld bytes: allocation failure forced by "
                        "PA_TEST_FAIL_ALLOC", (long long)plan.ws_bytes);
@@ -169,7 +190,7 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_po
                        hipGetErrorString(e));
   }
   const hipError_t e = pa::launch_decode(plan, ws, stream);
-  if (ws) (void)hipFreeAsync(ws, stream);
+  (void)hipFreeAsync(ws, stream);
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
   return PA_OK;
 }

@@ -71,8 +71,24 @@ struct Unpack<TF16> {
   }
 };
 
+// Read-only int32 data (block tables, context lengths) viewed through the
+// constant address space: a wave-uniform index then compiles to a scalar
+// load, whose wait (lgkmcnt) does not drain the vector loads in flight --
+// a vector load of a table entry would need vmcnt(0), which is in order and
+// so would wait for every K/V load issued before it.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) {
+  return (const_i32_ptr)(p);  // address-space cast
+}
+
 __device__ __forceinline__ u32x4_t load16(const uint8_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Streaming load for data read once (the KV cache in decode): the
+// nontemporal hint keeps it from displacing reusable lines in the caches.
+__device__ __forceinline__ u32x4_t load16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
 // DPP move within rows of 16 lanes.  quad_perm(1,0,3,2) = 0xB1,

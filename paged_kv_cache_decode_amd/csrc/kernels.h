@@ -8,9 +8,13 @@
 
 namespace pa {
 
-// Launches the partition kernel and, when a sequence can span several
-// partitions, the log-sum-exp merge.  `workspace` holds ws_bytes bytes.
+// Launches the partition kernel and the log-sum-exp merge.  `workspace`
+// holds plan.ws_bytes bytes.
 hipError_t launch_decode(const DecodePlan& plan, void* workspace, hipStream_t stream);
+
+// Wavefronts of the decode kernel the current device keeps resident for
+// this instance (falls back to an MI355X's 256 CUs x 12 without a device).
+int decode_worker_count(int dtype, int D, int G);
 
 hipError_t launch_prefill(const PrefillPlan& plan, hipStream_t stream);
 

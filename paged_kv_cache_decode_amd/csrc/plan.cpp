@@ -141,34 +141,18 @@ bool ranges_overlap(const pa_tensor* a, const pa_tensor* b) {
 
 }  // namespace
 
-int partition_override_from_env() {
-  const char* s = std::getenv("PA_PARTITION_TOKENS");
+int workers_override_from_env() {
+  const char* s = std::getenv("PA_DECODE_WORKERS");
   if (!s || !*s) return 0;
   char* end = nullptr;
   long v = std::strtol(s, &end, 10);
-  if (*end || v <= 0 || v % 64 || v > kMaxPartition) return -1;
+  if (*end || v <= 0 || v > kMaxWorkers) return -1;
   return static_cast<int>(v);
-}
-
-int choose_partition(int S, int Hkv, int max_context, int override_tokens) {
-  if (override_tokens > 0) return override_tokens;
-  // Aim at roughly 2048 partition workgroups for the longest possible
-  // contexts (8 per CU on a 256-CU part) so that long sequences are split
-  // finely enough to balance, without making partitions so short that the
-  // merge traffic matters.  Partitions are whole multiples of 64 keys (one
-  // 16-key tile per wave per round) between 256 and 4096 keys.
-  const double units = static_cast<double>(S) * Hkv;
-  double want = units > 0 ? static_cast<double>(max_context) * units / 2048.0 : 4096.0;
-  int64_t p = static_cast<int64_t>(std::ceil(want / 64.0)) * 64;
-  if (p < 256) p = 256;
-  if (p > kMaxPartition) p = kMaxPartition;
-  return static_cast<int>(p);
 }
 
 int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
                 const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
-                const pa_tensor* out, int partition_override, DecodePlan* plan,
-                std::string* err) {
+                const pa_tensor* out, int workers, DecodePlan* plan, std::string* err) {
   int st;
   if ((st = check_rows(q, "q", err))) return st;
   if ((st = check_pools(k_pool, v_pool, err))) return st;
@@ -218,10 +202,14 @@ int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_
     return fail(err, PA_ERR_UNSUPPORTED, "more than 65535 sequences or KV heads");
   if (MB * B > (int64_t)1 << 30)
     return fail(err, PA_ERR_UNSUPPORTED, "table covers more than 2^30 keys");
-  if (partition_override < 0)
-    return fail(err, PA_ERR_ARG,
-                "PA_PARTITION_TOKENS must be a positive multiple of 64 up to %d",
-                kMaxPartition);
+  if (B * Hkv * D * 4 >= ((int64_t)1 << 31))
+    return fail(err, PA_ERR_UNSUPPORTED, "a pool block must be smaller than 2^31 bytes");
+  if (workers <= 0 || workers > kMaxWorkers)
+    return fail(err, PA_ERR_ARG, "decode worker count must be in 1..%d (PA_DECODE_WORKERS)",
+                kMaxWorkers);
+  const int64_t tiles_bound = S * Hkv * ((MB * B + kTileKeys - 1) / kTileKeys);
+  if (tiles_bound >= ((int64_t)1 << 40))
+    return fail(err, PA_ERR_UNSUPPORTED, "more than 2^40 key tiles");
 
   DecodePlan p;
   p.dtype = q->dtype;
@@ -229,15 +217,15 @@ int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_
   p.S = (int)S; p.H = (int)H; p.Hkv = (int)Hkv; p.G = (int)G; p.D = (int)D; p.B = (int)B;
   p.MB = (int)MB;
   p.NB = NB;
-  const int max_ctx = (int)(MB * B);
-  p.P = choose_partition((int)S, (int)Hkv, max_ctx, partition_override);
-  p.MP = (int)((max_ctx + p.P - 1) / p.P);
-  if (p.MP < 1) p.MP = 1;
-  p.grid[0] = p.MP;
-  p.grid[1] = Hkv;
-  p.grid[2] = S;
+  p.workers = workers;
+  p.slots = (int64_t)workers + S * Hkv;
   p.block_threads = 64 * kDecodeWaves;
-  p.ws_bytes = p.MP > 1 ? S * H * (int64_t)p.MP * (D + 1) * 4 : 0;
+  // Workgroups, rounded up to a multiple of the 8 XCDs (see the kernel).
+  p.grid[0] = ((workers + kDecodeWaves - 1) / kDecodeWaves + 7) / 8 * 8;
+  p.grid[1] = 1;
+  p.grid[2] = 1;
+  // part_o [slots, G, D] f32 | part_lse [slots, G] f32 | unit ranges [S*Hkv] int2
+  p.ws_bytes = p.slots * G * D * 4 + p.slots * G * 4 + S * Hkv * 8;
   p.q = q->data; p.q_ss = q->stride[0]; p.q_sh = q->stride[1];
   p.k = k_pool->data; p.v = v_pool->data;
   p.bt = static_cast<const int32_t*>(block_table->data); p.bt_ss = block_table->stride[0];

@@ -12,23 +12,25 @@
 
 namespace pa {
 
-// Decode partition kernel geometry: each workgroup has kDecodeWaves
-// wavefronts of 64 lanes and processes one partition of P keys for one
-// (sequence, KV head); a wavefront handles 16-key tiles.
+// Decode geometry.  The decode kernel runs a fixed set of "workers" (one
+// wavefront each, kDecodeWaves per workgroup); all (sequence, KV head)
+// units' 16-key tiles form one list that is cut into equal contiguous
+// slices, one per worker.  A worker's piece of one unit is a partition;
+// units split over several workers are joined by the merge kernel.
 constexpr int kDecodeWaves = 4;
 constexpr int kTileKeys = 16;
-constexpr int kMaxPartition = 64 * kTileKeys * kDecodeWaves;  // 4096 keys
+constexpr int kMaxWorkers = 1 << 20;
 
 struct DecodePlan {
   int dtype = 0;      // pa_dtype of q / pools
   int out_dtype = 0;  // PA_F32 or dtype
   int S = 0, H = 0, Hkv = 0, G = 0, D = 0, B = 0, MB = 0;
   int64_t NB = 0;
-  int P = 0;   // keys per partition
-  int MP = 0;  // max partitions per sequence
+  int workers = 0;       // wavefronts launched
+  int64_t slots = 0;     // partial-result slots: workers + S * Hkv
   int64_t grid[3] = {0, 0, 0};
   int block_threads = 0;
-  int64_t ws_bytes = 0;  // partial outputs + log-sum-exp, 0 when MP == 1
+  int64_t ws_bytes = 0;  // partial outputs, log-sum-exp and per-unit ranges
   // operands
   const void* q = nullptr;
   int64_t q_ss = 0, q_sh = 0;  // strides (elements) over sequence and head
@@ -79,13 +81,11 @@ struct WriteKvPlan {
   void* vp = nullptr;
 };
 
-// Partition size for decode from host shapes (and PA_PARTITION_TOKENS).
-int choose_partition(int S, int Hkv, int max_context, int override_tokens);
-
+// Validates the decode arguments and sizes the launch for `workers`
+// wavefronts (the device's resident capacity, or an override).
 int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
                 const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
-                const pa_tensor* out, int partition_override, DecodePlan* plan,
-                std::string* err);
+                const pa_tensor* out, int workers, DecodePlan* plan, std::string* err);
 
 int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
                  const pa_tensor* block_table, const pa_tensor* context_lens,
@@ -96,7 +96,7 @@ int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
                   const pa_tensor* slot_mapping, const pa_tensor* k_pool,
                   const pa_tensor* v_pool, WriteKvPlan* plan, std::string* err);
 
-// Reads PA_PARTITION_TOKENS; 0 when unset.  Returns -1 when set but invalid.
-int partition_override_from_env();
+// Reads PA_DECODE_WORKERS (1 .. kMaxWorkers); 0 when unset, -1 when invalid.
+int workers_override_from_env();
 
 }  // namespace pa

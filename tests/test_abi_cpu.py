@@ -127,32 +127,35 @@ def test_decode_rejects_nan_scale():
     assert call_decode(decode_args(), scale=float("nan")) == -8
 
 
-def test_decode_plan_math():
+def test_decode_plan_math(monkeypatch):
+    monkeypatch.delenv("PA_DECODE_WORKERS", raising=False)
     st, info = plan(decode_args(S=64, MB=256))
     assert st == 0
-    assert info.partition_tokens % 64 == 0
-    assert info.max_partitions == -(-256 * 16 // info.partition_tokens)
-    assert tuple(info.grid) == (info.max_partitions, 8, 64)
-    assert info.block_threads == 256
-    assert info.workspace_bytes == (64 * 32 * info.max_partitions * 129 * 4
-                                    if info.max_partitions > 1 else 0)
+    W = info.workers
+    assert W > 0 and info.waves_per_group == 4 and info.block_threads == 256
+    assert tuple(info.grid) == (-(-W // 32) * 8, 1, 1)  # groups, a multiple of 8
+    G, d, S, Hkv = 4, 128, 64, 8
+    slots = W + S * Hkv
+    assert info.workspace_bytes == slots * G * d * 4 + slots * G * 4 + S * Hkv * 8
     # A long-context shape: 4 x 100,000 keys (6,250 blocks of 16); 64-bit sizes.
     st, info = plan(decode_args(S=4, MB=6250, NB=31250))
-    assert st == 0 and info.max_partitions > 1
+    assert st == 0
 
 
-def test_partition_override(monkeypatch):
-    monkeypatch.setenv("PA_PARTITION_TOKENS", "512")
+def test_worker_override(monkeypatch):
+    monkeypatch.setenv("PA_DECODE_WORKERS", "7")
     st, info = plan(decode_args(S=2, MB=64))
-    assert st == 0 and info.partition_tokens == 512 and info.max_partitions == 2
-    monkeypatch.setenv("PA_PARTITION_TOKENS", "100")
+    assert st == 0 and info.workers == 7 and tuple(info.grid) == (8, 1, 1)
+    monkeypatch.setenv("PA_DECODE_WORKERS", "0")
+    assert plan(decode_args())[0] == -8
+    monkeypatch.setenv("PA_DECODE_WORKERS", "x")
     assert plan(decode_args())[0] == -8
 
 
 def test_forced_alloc_failure(monkeypatch):
     """The workspace-allocation failure path, forced from the host."""
     monkeypatch.setenv("PA_TEST_FAIL_ALLOC", "1")
-    monkeypatch.setenv("PA_PARTITION_TOKENS", "256")
+    monkeypatch.setenv("PA_DECODE_WORKERS", "64")
     a = decode_args(S=2, MB=64)
     assert call_decode(a) == -6
     assert "PA_TEST_FAIL_ALLOC" in B.lib().pa_last_error().decode()
