@@ -68,6 +68,8 @@ struct PrefillPlan {
 
 // Query positions per prefill workgroup (all G heads of one KV head).
 constexpr int kPrefillRows = 64;
+// Waves per query head in a prefill workgroup (each wave owns 32 positions).
+constexpr int kPrefillRowWaves = kPrefillRows / 32;
 
 struct WriteKvPlan {
   int dtype = 0;

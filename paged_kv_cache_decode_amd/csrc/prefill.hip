@@ -9,12 +9,15 @@
 // skipped).
 //
 // Work decomposition:
-//   workgroup = 64 query positions x the G query heads of one KV head
-//   (2G waves; a wave owns 32 positions of one head).  K/V tiles of 64 keys
-//   are gathered once per workgroup into LDS and feed all G heads.
-//   Key tiles wholly above the diagonal are never loaded.
+//   workgroup = kPrefillRows query positions x the G query heads of one KV
+//   head (a wave owns 32 positions of one head).  K/V tiles of 64 keys
+//   are gathered once per workgroup into LDS and feed all G heads.  Key
+//   tiles wholly above the diagonal are never loaded.  LDS is double
+//   buffered: while the waves compute on one tile the next one is written
+//   to the other buffer from registers, and the tile after that is already
+//   being fetched, so there is one barrier per tile.
 //
-// Per 64-key tile a wave computes, on 32x32x16 MFMAs:
+// Per 32-key half of a 64-key tile a wave computes, on 32x32x16 MFMAs:
 //   S^T = K Q^T   (A = K from LDS, B = Q from registers; bf16/f16 inputs,
 //                  fp32 accumulate).  The transposed product leaves every
 //                  score of query row r in lane r (and r + 32), so the
@@ -23,25 +26,35 @@
 //                  rounded to fp16; fp32 accumulate).  V is written to LDS
 //                  transposed (d-major) and converted to fp16 while it is
 //                  staged; fp16 keeps P's rounding error 8x below bf16's.
-//   O^T's layout again keeps row r in lane r, so the softmax rescale is a
-//   per-lane multiply.
+// Softmax: the scale is folded into the exponent's FMA (p = 2^(s*c - m)
+// with c = scale*log2 e); the running maximum is only raised when a row's
+// new maximum exceeds it by more than 2^8 (p then stays below 256, exact
+// in fp16's range), so the O rescale is rare; row sums accumulate the
+// fp16 P values with v_dot2, consistent with what the P.V product uses.
+// Only tiles that cross the diagonal (or the end of the context) run the
+// masking code.
 //
 // Workgroups are ordered so that each XCD (8 per MI355X, fed round-robin)
 // works through a contiguous slice of (KV head, sequence, query tile), with
 // a sequence's query tiles longest-first; the tiles running together on an
 // XCD then share the same K/V in its L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace pa {
 namespace {
 
-constexpr int kBN = 64;                  // keys per tile
-constexpr int kD = 128;                  // head size
-constexpr int kKRow = kD * 2 + 16;       // K tile row in LDS (bytes, padded)
-constexpr int kVRow = kBN * 2 + 8;       // V^T tile row in LDS (bytes, padded)
-constexpr int kKChunks = kBN * kD * 2 / 16;  // 16-byte chunks in a K tile (1024)
+constexpr int kBN = 64;                        // keys per tile
+constexpr int kD = 128;                        // head size
+constexpr int kKRow = kD * 2 + 16;             // K tile row in LDS (bytes, padded)
+constexpr int kVRow = kBN * 2 + 8;             // V^T tile row in LDS (bytes, padded)
+constexpr int kKBytes = kBN * kKRow;           // one K tile in LDS
+constexpr int kVBytes = kD * kVRow;            // one V^T tile in LDS
+constexpr int kKChunks = kBN * kD * 2 / 16;    // 16-byte chunks in a K tile (1024)
 constexpr int kVUnits = (kBN / 2) * (kD / 8);  // (key pair, 8-column) units (512)
+constexpr float kRescaleSlack = 8.f;           // lazy-rescale threshold (log2 units)
 
 struct PrefillArgs {
   const uint8_t* q;
@@ -55,10 +68,11 @@ struct PrefillArgs {
   void* out;
   int64_t o_st, o_sh;  // elements
   int out_f32;
-  int S, Hkv, q_tiles, bs_shift, causal;
-  int64_t n_wg;      // real workgroups (q_tiles * Hkv * S)
+  int S, Hkv, MB, q_tiles, bs_shift, causal;
+  uint32_t q_sign;     // XORed into Q's 16-bit lanes (0x80008000 when scale < 0)
+  int64_t n_wg;        // real workgroups (q_tiles * Hkv * S)
   int64_t wg_per_xcd;  // ceil(n_wg / 8)
-  float scale_log2;
+  float c;             // |scale| * log2(e)
 };
 
 template <class T>
@@ -84,7 +98,7 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// Low / high 16-bit element of a storage dword, as fp16 bits.
+// Low / high 16-bit element of two storage dwords, as one fp16 pair.
 template <class T>
 __device__ __forceinline__ uint32_t pair_to_f16(uint32_t w0, uint32_t w1, bool high) {
   if constexpr (__is_same(T, TF16)) {
@@ -94,15 +108,20 @@ __device__ __forceinline__ uint32_t pair_to_f16(uint32_t w0, uint32_t w1, bool h
   }
 }
 
+// V^T rows are stored with their key-pair columns XOR-swizzled by the row's
+// 32-row group (even values, so the two dwords of a 4-key read stay
+// adjacent); it spreads the transposing writes over the LDS banks.
+__device__ __forceinline__ int vt_col(int d, int kp) { return kp ^ ((d >> 5) << 1); }
+
 template <class T, int G>
-__global__ __launch_bounds__(128 * G) void prefill_kernel(PrefillArgs a) {
-  constexpr int kNT = 128 * G;  // threads
+__global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(PrefillArgs a) {
+  constexpr int kNT = 64 * kPrefillRowWaves * G;  // threads
   constexpr int kKPer = kKChunks / kNT;
   constexpr int kVPer = kVUnits / kNT;
   static_assert(kKPer * kNT == kKChunks && kVPer * kNT == kVUnits, "tile split");
 
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBN * kKRow];
-  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kD * kVRow];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kKBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[2][kVBytes];
 
   // XCD-aware order: hardware workgroup b runs on XCD b % 8; give each XCD
   // a contiguous slice of the logical order (g, s, query tile descending).
@@ -115,16 +134,17 @@ __global__ __launch_bounds__(128 * G) void prefill_kernel(PrefillArgs a) {
   const int s = rem / a.q_tiles;
   const int qt = a.q_tiles - 1 - rem % a.q_tiles;
 
-  const int q0 = a.qsl[s];
-  const int L = a.qsl[s + 1] - q0;
-  const int n = a.cl[s];
+  const const_i32_ptr qsl = as_const(a.qsl);
+  const int q0 = qsl[s];
+  const int L = qsl[s + 1] - q0;
+  const int n = as_const(a.cl)[s];
   if (qt * kPrefillRows >= L) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int hl = w % G;          // head within the group
-  const int half = w / G;        // which 32 of the 64 positions
+  const int hl = w % G;    // head within the group
+  const int half = w / G;  // which 32 of the 64 positions
   const int hq = g * G + hl;
   const int r32 = lane & 31;
   const int hi = lane >> 5;
@@ -139,11 +159,14 @@ __global__ __launch_bounds__(128 * G) void prefill_kernel(PrefillArgs a) {
   int kend = n;
   if (a.causal) kend = min(n, shift + min(qt * kPrefillRows + kPrefillRows, L));
   const int ntk = (kend + kBN - 1) / kBN;
-  // Keys visible to this wave's first / last valid row.
-  const int wave_last_i = min(row0 + 31, L - 1);
+  // Per wave: tiles below `full` need no mask; tiles from `full` up to
+  // `last` need one; later tiles hold no visible key for this wave.
   const bool wave_active = row0 < L;
+  const int wave_last_i = min(row0 + 31, L - 1);
   const int vis_lo = a.causal ? shift + row0 : n - 1;         // first row's last key
   const int vis_hi = a.causal ? shift + wave_last_i : n - 1;  // last row's last key
+  const int full = min(vis_lo + 1, n) / kBN;                  // fully visible tiles
+  const int last = wave_active ? vis_hi / kBN : -1;
   const int my_vis = a.causal ? shift + my_i : n - 1;
 
   // Q^T as the MFMA B operand: lane holds row r32, columns ks*16 + 8*hi.
@@ -151,24 +174,32 @@ __global__ __launch_bounds__(128 * G) void prefill_kernel(PrefillArgs a) {
   {
     const uint8_t* qrow = a.q + (int64_t)(q0 + my_i) * a.q_st + (int64_t)hq * a.q_sh + hi * 16;
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks)
+    for (int ks = 0; ks < kD / 16; ++ks) {
       qf[ks] = row_ok ? load16(qrow + ks * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      qf[ks] ^= a.q_sign;
+    }
   }
 
-  const int32_t* bt_row = a.bt + (int64_t)s * a.bt_ss;
+  const const_i32_ptr bt_row = as_const(a.bt) + (int64_t)s * a.bt_ss;
   const int64_t tok_stride = (int64_t)a.Hkv * kD * 2;
   const int bmask = (1 << a.bs_shift) - 1;
   const uint8_t* kbase = a.k + (int64_t)g * kD * 2;
   const uint8_t* vbase = a.v + (int64_t)g * kD * 2;
 
-  auto key_addr = [&](const uint8_t* base, int key) -> const uint8_t* {
-    const int phys = bt_row[key >> a.bs_shift];
-    return base + ((int64_t)phys << a.bs_shift) * tok_stride + (int64_t)(key & bmask) * tok_stride;
-  };
-
+  // Global -> registers for tile kt.  The (up to four) physical blocks of
+  // the tile come from scalar reads of the table; each thread picks its own.
   u32x4_t kreg[kKPer];
   u32x4_t vreg[kVPer][2];
   auto load_tile = [&](int kt) {
+    const int blk0 = (kt * kBN) >> a.bs_shift;
+    int phys[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) phys[b] = bt_row[min(blk0 + b, a.MB - 1)];
+    auto key_addr = [&](const uint8_t* base, int key) -> const uint8_t* {
+      const int b = (key >> a.bs_shift) - blk0;  // 0..3
+      const int p = b == 0 ? phys[0] : b == 1 ? phys[1] : b == 2 ? phys[2] : phys[3];
+      return base + ((int64_t)p << a.bs_shift) * tok_stride + (int64_t)(key & bmask) * tok_stride;
+    };
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
       const int chunk = tid + j * kNT;
@@ -187,23 +218,27 @@ __global__ __launch_bounds__(128 * G) void prefill_kernel(PrefillArgs a) {
                                     : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
-  auto store_tile = [&]() {
+  // Registers -> LDS buffer `buf` (K row-major, V transposed to fp16).
+  auto store_tile = [&](int buf) {
+    uint8_t* kl = k_lds[buf];
+    uint8_t* vl = vt_lds[buf];
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
       const int chunk = tid + j * kNT;
-      *reinterpret_cast<u32x4_t*>(k_lds + (chunk >> 4) * kKRow + (chunk & 15) * 16) = kreg[j];
+      *reinterpret_cast<u32x4_t*>(kl + (chunk >> 4) * kKRow + (chunk & 15) * 16) = kreg[j];
     }
 #pragma unroll
     for (int j = 0; j < kVPer; ++j) {
       const int u = tid + j * kNT;
-      const int kp = u >> 4;         // key pair
-      const int d0 = (u & 15) * 8;   // first of 8 columns
+      const int kp = u >> 4;        // key pair
+      const int d0 = (u & 15) * 8;  // first of 8 columns
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = pair_to_f16<T>(vreg[j][0][i], vreg[j][1][i], false);
-        const uint32_t hv = pair_to_f16<T>(vreg[j][0][i], vreg[j][1][i], true);
-        *reinterpret_cast<uint32_t*>(vt_lds + (d0 + 2 * i) * kVRow + kp * 4) = lo;
-        *reinterpret_cast<uint32_t*>(vt_lds + (d0 + 2 * i + 1) * kVRow + kp * 4) = hv;
+        const int d = d0 + 2 * i;
+        *reinterpret_cast<uint32_t*>(vl + d * kVRow + vt_col(d, kp) * 4) =
+            pair_to_f16<T>(vreg[j][0][i], vreg[j][1][i], false);
+        *reinterpret_cast<uint32_t*>(vl + (d + 1) * kVRow + vt_col(d + 1, kp) * 4) =
+            pair_to_f16<T>(vreg[j][0][i], vreg[j][1][i], true);
       }
     }
   };
@@ -213,86 +248,125 @@ __global__ __launch_bounds__(128 * G) void prefill_kernel(PrefillArgs a) {
   for (int md = 0; md < kD / 32; ++md)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[md][r] = 0.f;
-  float m_run = -INFINITY;  // running max of row r32 (log2 units)
-  float l_lane = 0.f;       // running sum over this lane's keys
+  float m_run = -INFINITY;  // running max of row r32, scaled (log2 units)
+  float l_lane = 0.f;       // running sum of this lane's P values
 
-  if (ntk > 0) load_tile(0);
-  for (int kt = 0; kt < ntk; ++kt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < ntk) load_tile(kt + 1);
-
-    const int kbase_t = kt * kBN;
-    if (!wave_active || kbase_t > vis_hi) continue;  // nothing visible for this wave
-    const bool need_mask = kbase_t + kBN - 1 > vis_lo || kbase_t + kBN > n;
-
-    // S^T = K Q^T for the tile's two 32-key blocks.
-    f32x16_t sc[2];
+  // One 64-key tile of this wave as two 32-key halves, software-pipelined so
+  // that matrix-core and vector work overlap inside the wave: both halves'
+  // S^T = K Q^T MFMAs are issued first; the softmax of half 0 (VALU) then
+  // runs while half 1's QK^T executes, and the softmax of half 1 while half
+  // 0's O^T += V^T P^T executes.
+  f16x2_t ones;
+  ones[0] = ones[1] = static_cast<_Float16>(1.f);
+  auto qk_half = [&](const uint8_t* kl, int mb) {
+    // All fragments are read before the first MFMA, so each MFMA waits only
+    // for its own LDS read (a rolling lgkmcnt) rather than a full round trip.
+    const uint8_t* krow = kl + (mb * 32 + r32) * kKRow + hi * 16;
+    u32x4_t kf[kD / 16];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int ks = 0; ks < kD / 16; ++ks) kf[ks] = *reinterpret_cast<const u32x4_t*>(krow + ks * 32);
+    f32x16_t sc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[mb][r] = 0.f;
-      const uint8_t* krow = k_lds + (mb * 32 + r32) * kKRow + hi * 16;
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks)
-        sc[mb] = mfma_qk<T>(*reinterpret_cast<const u32x4_t*>(krow + ks * 32), qf[ks], sc[mb]);
-    }
-
-    // Online softmax for row r32; key of element (mb, r) is
-    // kbase_t + mb*32 + 8*(r/4) + 4*hi + r%4.
+    for (int ks = 0; ks < kD / 16; ++ks) sc = mfma_qk<T>(kf[ks], qf[ks], sc);
+    return sc;
+  };
+  // Online-softmax update for one half; returns P (fp16) as two MFMA B
+  // operands.  Element r of this lane is key kt*64 + mb*32 + 8*(r/4) +
+  // 4*hi + r%4.
+  auto softmax_half = [&](const f32x16_t& sc, int kt, int mb, auto mask_tag, u32x4_t* pf) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    bool vis[16];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sc[mb][r] * a.scale_log2;
-        if (need_mask) {
-          const int key = kbase_t + mb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key > my_vis) x = -INFINITY;
-        }
-        sc[mb][r] = x;
-        tmax = fmaxf(tmax, x);
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (kMask) {
+        const int key = kt * kBN + mb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        vis[r] = key <= my_vis;
+        tmax = fmaxf(tmax, vis[r] ? sc[r] : -INFINITY);
+      } else {
+        tmax = fmaxf(tmax, sc[r]);
       }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_lane *= alpha;
+    // Lazy rescale: raise the running max only when some row's new max is
+    // more than kRescaleSlack above it (p = 2^(s*c - m) then stays < 2^8).
+    const float m_cand = tmax * a.c;
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_cand);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_lane *= alpha;
+#pragma unroll
+      for (int md = 0; md < kD / 32; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[md][r] *= alpha;
+    }
+    const float neg_m = -m_run;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = 8 * qq + 2 * j;
+        float p0 = fast_exp2(fmaf(sc[r0], a.c, neg_m));
+        float p1 = fast_exp2(fmaf(sc[r0 + 1], a.c, neg_m));
+        if constexpr (kMask) {
+          p0 = vis[r0] ? p0 : 0.f;
+          p1 = vis[r0 + 1] ? p1 : 0.f;
+        }
+        const uint32_t pk = pack_f16(p0, p1);
+        pf[qq][j] = pk;
+        l_lane = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk), ones, l_lane, false);
+      }
+  };
+  // O^T += V^T P^T over one half's 32 keys.
+  auto pv_half = [&](const uint8_t* vl, int mb, const u32x4_t* pf) {
+    u32x4_t vf[kD / 32][2];
+#pragma unroll
+    for (int md = 0; md < kD / 32; ++md) {
+      const int d = md * 32 + r32;
+      const uint8_t* vrow = vl + d * kVRow;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int kp = (mb * 32 + 16 * qq + 4 * hi) >> 1;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + vt_col(d, kp) * 4);
+        const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(vrow + vt_col(d, kp + 4) * 4);
+        vf[md][qq] = u32x4_t{lo[0], lo[1], hv[0], hv[1]};
+      }
+    }
 #pragma unroll
     for (int md = 0; md < kD / 32; ++md)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[md][r] *= alpha;
+      for (int qq = 0; qq < 2; ++qq) acc_o[md] = mfma_pv(vf[md][qq], pf[qq], acc_o[md]);
+  };
+  auto compute_tile = [&](int kt, int buf, auto mask_tag) {
+    const uint8_t* kl = k_lds[buf];
+    const uint8_t* vl = vt_lds[buf];
+    const f32x16_t sc0 = qk_half(kl, 0);
+    const f32x16_t sc1 = qk_half(kl, 1);
+    u32x4_t pf0[2], pf1[2];
+    softmax_half(sc0, kt, 0, mask_tag, pf0);
+    pv_half(vl, 0, pf0);
+    softmax_half(sc1, kt, 1, mask_tag, pf1);
+    pv_half(vl, 1, pf1);
+  };
 
-    u32x4_t pf[2][2];  // B operand of P^T per (mb, qq)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = fast_exp2(sc[mb][8 * qq + j] - m_new);
-          l_lane += pv[j];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pf[mb][qq][j] = pack_f16(pv[2 * j], pv[2 * j + 1]);
-      }
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int md = 0; md < kD / 32; ++md) {
-      const uint8_t* vrow = vt_lds + (md * 32 + r32) * kVRow;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          const int k0 = mb * 32 + 16 * qq + 4 * hi;
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + k0 * 2);
-          const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(vrow + (k0 + 8) * 2);
-          const u32x4_t av = {lo[0], lo[1], hv[0], hv[1]};
-          acc_o[md] = mfma_pv(av, pf[mb][qq], acc_o[md]);
-        }
+  if (ntk > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (ntk > 1) load_tile(1);
+  }
+  for (int kt = 0; kt < ntk; ++kt) {
+    __syncthreads();  // tile kt is in buffer kt & 1; buffer (kt+1) & 1 is free
+    if (kt + 1 < ntk) {
+      store_tile((kt + 1) & 1);
+      if (kt + 2 < ntk) load_tile(kt + 2);
+    }
+    if (kt < full) {
+      compute_tile(kt, kt & 1, std::false_type{});
+    } else if (kt <= last) {
+      compute_tile(kt, kt & 1, std::true_type{});
     }
   }
 
@@ -326,20 +400,20 @@ __global__ __launch_bounds__(128 * G) void prefill_kernel(PrefillArgs a) {
 }
 
 template <class T, int G>
-hipError_t launch_prefill_t(const PrefillPlan& pl, const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = a.wg_per_xcd * 8;
   KernelTimer t("prefill", stream);
-  hipLaunchKernelGGL((prefill_kernel<T, G>), dim3((unsigned)blocks), dim3(128 * G), 0, stream,
-                     a);
+  hipLaunchKernelGGL((prefill_kernel<T, G>), dim3((unsigned)blocks),
+                     dim3(64 * kPrefillRowWaves * G), 0, stream, a);
   return hipGetLastError();
 }
 
 template <class T>
 hipError_t dispatch_group(const PrefillPlan& pl, const PrefillArgs& a, hipStream_t stream) {
   switch (pl.G) {
-    case 1: return launch_prefill_t<T, 1>(pl, a, stream);
-    case 2: return launch_prefill_t<T, 2>(pl, a, stream);
-    case 4: return launch_prefill_t<T, 4>(pl, a, stream);
+    case 1: return launch_prefill_t<T, 1>(a, stream);
+    case 2: return launch_prefill_t<T, 2>(a, stream);
+    case 4: return launch_prefill_t<T, 4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -363,12 +437,16 @@ hipError_t launch_prefill(const PrefillPlan& pl, hipStream_t stream) {
   a.out_f32 = pl.out_dtype == PA_F32;
   a.S = pl.S;
   a.Hkv = pl.Hkv;
+  a.MB = pl.MB;
   a.q_tiles = pl.q_tiles;
   a.bs_shift = __builtin_ctz(pl.B);
   a.causal = pl.causal;
+  // A negative scale is applied by negating Q (exact in 16-bit formats) so
+  // that the softmax always works with c >= 0.
+  a.q_sign = pl.scale < 0.f ? 0x80008000u : 0u;
+  a.c = (pl.scale < 0.f ? -pl.scale : pl.scale) * 1.4426950408889634f;
   a.n_wg = (int64_t)pl.q_tiles * pl.Hkv * pl.S;
   a.wg_per_xcd = (a.n_wg + 7) / 8;
-  a.scale_log2 = pl.scale * 1.4426950408889634f;
   if (a.n_wg == 0) return hipSuccess;
   switch (pl.dtype) {
     case PA_F16: return dispatch_group<TF16>(pl, a, stream);
