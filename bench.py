@@ -52,6 +52,12 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) 10 times, to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--write-traffic", nargs=6, default=None,
+                    metavar=("KERNEL", "WORKLOAD", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                             "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of a "
+                         "workload run and of a --copy-calibration run into "
+                         "profiles/<KERNEL>_<WORKLOAD>_traffic.json (no GPU needed)")
     ap.add_argument("--only", default="",
                     help="comma list of workloads to run (for profiling): "
                          "gqa,long,prefix,prefill")
@@ -79,6 +85,51 @@ def load_traffic(kernel, workload, src_hash, bytes_per_launch):
             "ratio_to_algorithmic": round((rec["fetch_bytes"] + rec["write_bytes"]) /
                                           bytes_per_launch, 4),
             "scale_factor": rec.get("scale_factor"), "source": os.path.basename(path)}
+
+
+# Kernel (as the library's timer names it) -> (substring of its symbol, source).
+KERNEL_SOURCES = {"decode_partitions": ("decode_partitions_kernel", "decode.hip"),
+                  "prefill": ("prefill_kernel", "prefill.hip")}
+COPY_CALIBRATION_BYTES = 1 << 30
+
+
+def counter_mean_kib(path, name_part, counter):
+    """Mean per-dispatch value (KiB) of `counter` over dispatches whose kernel
+    symbol contains `name_part`, from a rocprofv3 counter_collection.csv."""
+    import csv
+    vals = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and name_part in row["Kernel_Name"]:
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for kernels matching {name_part!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """FETCH_SIZE / WRITE_SIZE per launch, each scaled by what the same
+    counter reports for a plain device copy of known size."""
+    part, src_file = KERNEL_SOURCES[kernel]
+    cf, _ = counter_mean_kib(copy_fetch_csv, "copyBuffer", "FETCH_SIZE")
+    cw, _ = counter_mean_kib(copy_write_csv, "copyBuffer", "WRITE_SIZE")
+    fetch_scale = COPY_CALIBRATION_BYTES / (cf * 1024.0)
+    write_scale = COPY_CALIBRATION_BYTES / (cw * 1024.0)
+    fk, nf = counter_mean_kib(fetch_csv, part, "FETCH_SIZE")
+    wk, nw = counter_mean_kib(write_csv, part, "WRITE_SIZE")
+    rec = {"kernel": kernel, "workload": workload, "source_hash": source_hash(src_file),
+           "fetch_bytes": round(fk * 1024.0 * fetch_scale),
+           "write_bytes": round(wk * 1024.0 * write_scale),
+           "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+           "dispatches": [nf, nw],
+           "scale_factor": {"fetch": round(fetch_scale, 4), "write": round(write_scale, 4)},
+           "calibration": "1 GiB device-to-device copy (bench.py --copy-calibration)"}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 class Timer:
@@ -148,6 +199,9 @@ def cpu_oracle_decode(case, budget_s=20.0):
 
 def main():
     a = parse()
+    if a.write_traffic:
+        write_traffic(*a.write_traffic)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the decode and "
               "prefill kernels shard by sequence or KV head with no exchange, and this build "
@@ -284,7 +338,11 @@ def main():
                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(ktf / BF16_PEAK_TFLOPS, 4),
                                   "kernel": "prefill_kernel<bf16,4>",
-                                  "kernel_avg_us": round(k_ms * 1e3, 2)}}
+                                  "kernel_avg_us": round(k_ms * 1e3, 2),
+                                  "traffic": load_traffic(
+                                      "prefill", "causal-bf16-prefill",
+                                      source_hash("prefill.hip"),
+                                      W.prefill_bytes(case))}}
             if not a.no_cpu_baseline:
                 import oracle
                 s0 = 1  # one prompt of the eight (515 tokens), all 32 heads

@@ -78,28 +78,25 @@ namespace pa {
 
 bool profiler_enabled() { return g_prof_on; }
 
-KernelTimer::KernelTimer(const char* name, hipStream_t stream) : name_(name), stream_(stream) {
+KernelTimer::KernelTimer(const char* name) : name_(name) {
   if (!g_prof_on) return;
-  if (hipEventCreate(&start_) != hipSuccess) {
-    start_ = nullptr;
-    return;
-  }
-  if (hipEventRecord(start_, stream_) != hipSuccess) {
+  if (hipEventCreate(&start_) != hipSuccess) start_ = nullptr;
+  if (start_ && hipEventCreate(&stop_) != hipSuccess) {
     (void)hipEventDestroy(start_);
-    start_ = nullptr;
+    start_ = stop_ = nullptr;
   }
 }
 
-KernelTimer::~KernelTimer() {
+void KernelTimer::commit() {
   if (!start_) return;
-  hipEvent_t stop = nullptr;
-  if (hipEventCreate(&stop) != hipSuccess || hipEventRecord(stop, stream_) != hipSuccess) {
-    if (stop) (void)hipEventDestroy(stop);
-    (void)hipEventDestroy(start_);
-    return;
-  }
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_pending.push_back({name_, start_, stop});
+  g_pending.push_back({name_, start_, stop_});
+  start_ = stop_ = nullptr;
+}
+
+KernelTimer::~KernelTimer() {
+  if (start_) (void)hipEventDestroy(start_);
+  if (stop_) (void)hipEventDestroy(stop_);
 }
 
 }  // namespace pa

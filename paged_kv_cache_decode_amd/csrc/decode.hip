@@ -44,6 +44,7 @@
 // is being used (about 5 us of loaded memory latency has to be covered).
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 
 #include <map>
 #include <mutex>
@@ -479,19 +480,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 
 template <class T, int D, int G>
 hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t stream) {
-  {
-    KernelTimer t("decode_partitions", stream);
-    hipLaunchKernelGGL((decode_partitions_kernel<T, D, G>), dim3((unsigned)pl.grid[0]),
-                       dim3(pl.block_threads), 0, stream, a);
-  }
-  hipError_t e = hipGetLastError();
+  const hipError_t e =
+      timed_launch("decode_partitions", decode_partitions_kernel<T, D, G>,
+                   dim3((unsigned)pl.grid[0]), dim3(pl.block_threads), stream, a);
   if (e != hipSuccess) return e;
-  {
-    KernelTimer t("decode_merge", stream);
-    hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(pl.H, pl.S), dim3(kMergeThreads), 0,
-                       stream, a);
-  }
-  return hipGetLastError();
+  return timed_launch("decode_merge", decode_merge_kernel<T, D, G>, dim3(pl.H, pl.S),
+                      dim3(kMergeThreads), stream, a);
 }
 
 template <class T, int D, int G>

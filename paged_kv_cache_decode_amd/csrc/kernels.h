@@ -20,14 +20,19 @@ hipError_t launch_prefill(const PrefillPlan& plan, hipStream_t stream);
 
 hipError_t launch_write_kv(const WriteKvPlan& plan, hipStream_t stream);
 
-// Kernel timer: while enabled, KernelTimer brackets a launch with events.
+// Kernel timer.  While the profiler is enabled, a KernelTimer holds a pair
+// of events that timed_launch (launch.h) binds to one kernel dispatch; the
+// pair is queued for reading by commit() and released otherwise.
 bool profiler_enabled();
 struct KernelTimer {
-  KernelTimer(const char* name, hipStream_t stream);
+  explicit KernelTimer(const char* name);
   ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+  void commit();
   const char* name_;
-  hipStream_t stream_;
   hipEvent_t start_ = nullptr;
+  hipEvent_t stop_ = nullptr;
 };
 
 }  // namespace pa

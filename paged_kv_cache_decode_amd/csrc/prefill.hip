@@ -42,6 +42,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace pa {
 namespace {
@@ -402,10 +403,8 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
 template <class T, int G>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = a.wg_per_xcd * 8;
-  KernelTimer t("prefill", stream);
-  hipLaunchKernelGGL((prefill_kernel<T, G>), dim3((unsigned)blocks),
-                     dim3(64 * kPrefillRowWaves * G), 0, stream, a);
-  return hipGetLastError();
+  return timed_launch("prefill", prefill_kernel<T, G>, dim3((unsigned)blocks),
+                      dim3(64 * kPrefillRowWaves * G), stream, a);
 }
 
 template <class T>

@@ -7,6 +7,7 @@
 // 16-byte piece of a K row and the same piece of the V row.
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace pa {
 namespace {
@@ -58,10 +59,8 @@ hipError_t launch_write_kv(const WriteKvPlan& pl, hipStream_t stream) {
   a.chunks = a.row_bytes / 16;
   const int64_t total = pl.N * pl.Hkv * a.chunks;
   if (total == 0) return hipSuccess;
-  KernelTimer t("write_kv", stream);
-  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, a);
-  return hipGetLastError();
+  return timed_launch("write_kv", write_kv_kernel, dim3((unsigned)((total + 255) / 256)),
+                      dim3(256), stream, a);
 }
 
 }  // namespace pa

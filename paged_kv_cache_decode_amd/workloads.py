@@ -314,6 +314,20 @@ def decode_bytes(case: PagedCase, out_bytes_per_elem: int) -> int:
     return kv + qo + tab
 
 
+def prefill_bytes(case: PagedCase, out_bytes_per_elem: int = 2) -> int:
+    """Compulsory HBM bytes of one prefill call: Q and O once, each context
+    token's K and V rows once per KV head, the context lengths, the query
+    start offsets and the table entries that cover the contexts."""
+    T, H, d = case.q.shape
+    Hkv = case.k_pool.shape[2]
+    B = case.k_pool.shape[1]
+    esz = case.q.dtype.itemsize
+    keys = int(case.context_lens.astype(np.int64).sum())
+    blocks = int(sum(-(-int(n) // B) for n in case.context_lens))
+    return (T * H * d * (esz + out_bytes_per_elem) + keys * Hkv * d * esz * 2 +
+            4 * (blocks + 2 * case.num_seqs + 1))
+
+
 def prefill_flops(case: PagedCase) -> int:
     """Algorithmic FLOPs of one prefill call: 4*d per visible (query, key)
     pair per head (2*d for Q.K, 2*d for P.V); exponentials not counted."""
