@@ -109,6 +109,16 @@ __device__ __forceinline__ uint32_t pair_to_f16(uint32_t w0, uint32_t w1, bool h
   }
 }
 
+// The value of lane l ^ 32 (v_permlane32_swap exchanges the wave's halves
+// without going through LDS).
+__device__ __forceinline__ float swap_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // r[0] holds the low half in both halves, r[1] the high half.
+  const bool upper = (threadIdx.x & 32) != 0;
+  return __builtin_bit_cast(float, upper ? r[0] : r[1]);
+}
+
 // V^T rows are stored with their key-pair columns XOR-swizzled by the row's
 // 32-row group (even values, so the two dwords of a 4-key read stay
 // adjacent); it spreads the transposing writes over the LDS banks.
@@ -182,51 +192,65 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   }
 
   const const_i32_ptr bt_row = as_const(a.bt) + (int64_t)s * a.bt_ss;
-  const int64_t tok_stride = (int64_t)a.Hkv * kD * 2;
+  const int tok_stride = a.Hkv * kD * 2;  // bytes between consecutive slots
   const int bmask = (1 << a.bs_shift) - 1;
+  const int64_t block_bytes = (int64_t)tok_stride << a.bs_shift;
   const uint8_t* kbase = a.k + (int64_t)g * kD * 2;
   const uint8_t* vbase = a.v + (int64_t)g * kD * 2;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index (uniform)
+  // Gather addressing.  Every load instruction of a wave covers 4 (K) or 8
+  // (V) consecutive keys starting at a multiple of 4 (8), so all its lanes
+  // sit in one KV block (B >= 16): the block's address comes from one scalar
+  // table read and scalar arithmetic, and each lane adds a fixed offset.
+  // Key starts at or past the end are clamped to the last 4 keys before
+  // `kend` (a block the table maps); the rows they fetch are either masked
+  // (K) or zeroed before use (V).
+  const int kend_c = max(kend - 1, 0) & ~3;
+  const uint32_t k_lane = (uint32_t)((lane >> 4) * tok_stride + (lane & 15) * 16);
+  const uint32_t v_lane = (uint32_t)(2 * (lane >> 4) * tok_stride + (lane & 15) * 16);
+  auto row_addr = [&](const uint8_t* base, int key) -> const uint8_t* {
+    const int blk = key >> a.bs_shift;
+    const int64_t phys = bt_row[blk];
+    return base + phys * block_bytes + (int64_t)((key & bmask) * tok_stride);
+  };
 
-  // Global -> registers for tile kt.  The (up to four) physical blocks of
-  // the tile come from scalar reads of the table; each thread picks its own.
+  // Global -> registers for tile kt.
   u32x4_t kreg[kKPer];
   u32x4_t vreg[kVPer][2];
   auto load_tile = [&](int kt) {
-    const int blk0 = (kt * kBN) >> a.bs_shift;
-    int phys[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) phys[b] = bt_row[min(blk0 + b, a.MB - 1)];
-    auto key_addr = [&](const uint8_t* base, int key) -> const uint8_t* {
-      const int b = (key >> a.bs_shift) - blk0;  // 0..3
-      const int p = b == 0 ? phys[0] : b == 1 ? phys[1] : b == 2 ? phys[2] : phys[3];
-      return base + ((int64_t)p << a.bs_shift) * tok_stride + (int64_t)(key & bmask) * tok_stride;
-    };
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
-      const int chunk = tid + j * kNT;
-      const int key = kt * kBN + (chunk >> 4);
-      kreg[j] = key < kend ? load16(key_addr(kbase, key) + (chunk & 15) * 16)
-                           : u32x4_t{0u, 0u, 0u, 0u};
+      const int kb = min(kt * kBN + 4 * wu + j * (kNT / 16), kend_c);
+      kreg[j] = load16(row_addr(kbase, kb) + k_lane);
     }
 #pragma unroll
     for (int j = 0; j < kVPer; ++j) {
-      const int u = tid + j * kNT;
-      const int key = kt * kBN + 2 * (u >> 4);
-      const int col = (u & 15) * 16;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        vreg[j][t] = key + t < kend ? load16(key_addr(vbase, key + t) + col)
-                                    : u32x4_t{0u, 0u, 0u, 0u};
+      const int kb = min(kt * kBN + 8 * wu + j * (kNT / 8), kend_c & ~7);
+      const uint8_t* p = row_addr(vbase, kb) + v_lane;
+      vreg[j][0] = load16(p);
+      vreg[j][1] = load16(p + tok_stride);
     }
   };
-  // Registers -> LDS buffer `buf` (K row-major, V transposed to fp16).
-  auto store_tile = [&](int buf) {
+  // Registers -> LDS buffer `buf` (K row-major, V transposed to fp16).  In
+  // the tile that reaches `kend`, V rows at or past it are zeroed first (they
+  // may be clamped duplicates or unwritten slots; P is zero there, and a
+  // zero row keeps the product finite).
+  auto store_tile = [&](int kt, int buf) {
     uint8_t* kl = k_lds[buf];
     uint8_t* vl = vt_lds[buf];
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
       const int chunk = tid + j * kNT;
       *reinterpret_cast<u32x4_t*>(kl + (chunk >> 4) * kKRow + (chunk & 15) * 16) = kreg[j];
+    }
+    if ((kt + 1) * kBN > kend) {
+#pragma unroll
+      for (int j = 0; j < kVPer; ++j) {
+        const int key = kt * kBN + 2 * ((tid + j * kNT) >> 4);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (key + t >= kend) vreg[j][t] = u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int j = 0; j < kVPer; ++j) {
@@ -259,19 +283,32 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   // 0's O^T += V^T P^T executes.
   f16x2_t ones;
   ones[0] = ones[1] = static_cast<_Float16>(1.f);
-  auto qk_half = [&](const uint8_t* kl, int mb) {
-    // All fragments are read before the first MFMA, so each MFMA waits only
-    // for its own LDS read (a rolling lgkmcnt) rather than a full round trip.
-    const uint8_t* krow = kl + (mb * 32 + r32) * kKRow + hi * 16;
-    u32x4_t kf[kD / 16];
+  // S^T = K Q^T for both 32-key halves of a tile.  The schedule is pinned:
+  // half 0's eight K fragments are read first, then each half-0 MFMA is
+  // followed by the read of one half-1 fragment, then half 1's MFMAs; every
+  // MFMA then finds its operand already in registers.
+  auto qk_tile = [&](const uint8_t* kl, f32x16_t& sc0, f32x16_t& sc1) {
+    const uint8_t* krow = kl + r32 * kKRow + hi * 16;
+    u32x4_t kf0[kD / 16], kf1[kD / 16];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) kf[ks] = *reinterpret_cast<const u32x4_t*>(krow + ks * 32);
-    f32x16_t sc;
+    for (int ks = 0; ks < kD / 16; ++ks)
+      kf0[ks] = *reinterpret_cast<const u32x4_t*>(krow + ks * 32);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+    for (int ks = 0; ks < kD / 16; ++ks)
+      kf1[ks] = *reinterpret_cast<const u32x4_t*>(krow + 32 * kKRow + ks * 32);
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) sc = mfma_qk<T>(kf[ks], qf[ks], sc);
-    return sc;
+    for (int r = 0; r < 16; ++r) sc0[r] = sc1[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) sc0 = mfma_qk<T>(kf0[ks], qf[ks], sc0);
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) sc1 = mfma_qk<T>(kf1[ks], qf[ks], sc1);
+    __builtin_amdgcn_sched_group_barrier(0x100, kD / 16, 0);  // DS reads, half 0
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA, half 0
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read, half 1
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kD / 16, 0);  // MFMAs, half 1
   };
   // Online-softmax update for one half; returns P (fp16) as two MFMA B
   // operands.  Element r of this lane is key kt*64 + mb*32 + 8*(r/4) +
@@ -290,7 +327,7 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
         tmax = fmaxf(tmax, sc[r]);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = fmaxf(tmax, swap_halves(tmax));
     // Lazy rescale: raise the running max only when some row's new max is
     // more than kRescaleSlack above it (p = 2^(s*c - m) then stays < 2^8).
     const float m_cand = tmax * a.c;
@@ -344,8 +381,8 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   auto compute_tile = [&](int kt, int buf, auto mask_tag) {
     const uint8_t* kl = k_lds[buf];
     const uint8_t* vl = vt_lds[buf];
-    const f32x16_t sc0 = qk_half(kl, 0);
-    const f32x16_t sc1 = qk_half(kl, 1);
+    f32x16_t sc0, sc1;
+    qk_tile(kl, sc0, sc1);
     u32x4_t pf0[2], pf1[2];
     softmax_half(sc0, kt, 0, mask_tag, pf0);
     pv_half(vl, 0, pf0);
@@ -355,13 +392,13 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
 
   if (ntk > 0) {
     load_tile(0);
-    store_tile(0);
+    store_tile(0, 0);
     if (ntk > 1) load_tile(1);
   }
   for (int kt = 0; kt < ntk; ++kt) {
     __syncthreads();  // tile kt is in buffer kt & 1; buffer (kt+1) & 1 is free
     if (kt + 1 < ntk) {
-      store_tile((kt + 1) & 1);
+      store_tile(kt + 1, (kt + 1) & 1);
       if (kt + 2 < ntk) load_tile(kt + 2);
     }
     if (kt < full) {
@@ -372,7 +409,7 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   }
 
   if (!row_ok) return;
-  const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+  const float l_tot = l_lane + swap_halves(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t obase = (int64_t)(q0 + my_i) * a.o_st + (int64_t)hq * a.o_sh;
 #pragma unroll
