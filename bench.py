@@ -6,10 +6,11 @@ Headline (the JSON line's ``value``): ``pa_decode`` on the batched GQA
 decode workload -- 64 sequences, 32 query / 8 KV heads, d = 128, context
 lengths uniform in [128, 4096], block size 16, fp16 -- as achieved HBM GB/s
 of algorithmic bytes (every attended K/V row once per KV head, q, out, the
-table entries used) per step.  One step = one ``pa_decode`` call (partition
-kernel + merge).  Inputs are resident in HBM; steps rotate over three copies
-of the pools so that the 256 MB Infinity Cache cannot hold the 0.55 GB of
-K/V between steps.
+table entries used) per step.  One step = one ``pa_decode`` call, which is
+one kernel (split units are merged by the wavefront that finishes their last
+partition).  Inputs are resident in HBM; steps rotate over three copies of
+the pools so that the 256 MB Infinity Cache cannot hold the 0.55 GB of K/V
+between steps.
 
 The same line carries:
 * ``roofline``: the partition kernel's algorithmic bytes / its average
@@ -172,12 +173,12 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype):
     timer.run(step, steps)
     binding.profiler_enable(False)
     part_ms, part_n = kernel_avg_ms(binding, "decode_partitions")
-    merge_ms, merge_n = kernel_avg_ms(binding, "decode_merge")
     binding.profiler_reset()
     del calls, devs
+    torch.cuda.synchronize()
+    binding.workspace_release()
     torch.cuda.empty_cache()
-    return dict(sec=sec, part_ms=part_ms, part_launches=part_n,
-                merge_ms=merge_ms if merge_n else 0.0, plan=plan)
+    return dict(sec=sec, part_ms=part_ms, part_launches=part_n, plan=plan)
 
 
 def cpu_oracle_decode(case, budget_s=20.0):
@@ -243,7 +244,6 @@ def main():
                 "traffic": load_traffic("decode_partitions", "gqa-f16-decode", src, nbytes),
                 "kernel": "decode_partitions_kernel<f16,128,4>",
                 "kernel_avg_us": round(r["part_ms"] * 1e3, 2),
-                "merge_avg_us": round(r["merge_ms"] * 1e3, 2),
                 "algorithmic_bytes_per_launch": nbytes}
         result = {
             "metric": "Paged attn: decode HBM GB/s (% of peak); causal prefill TFLOP/s "
@@ -288,7 +288,6 @@ def main():
                 "ms_per_step": round(r["sec"] * 1e3, 4),
                 "partition_kernel_GB/s": round(nbytes / (r["part_ms"] * 1e-3) / 1e9, 1),
                 "partition_kernel_avg_us": round(r["part_ms"] * 1e3, 2),
-                "merge_avg_us": round(r["merge_ms"] * 1e3, 2),
                 "decode_workers": r["plan"]["workers"],
                 "algorithmic_bytes": nbytes}
             del case

@@ -105,9 +105,18 @@ typedef struct pa_tensor {
  * capacity): the 16-key tiles of all (sequence, KV head) pairs form one list
  * that is cut into W equal contiguous slices, so long contexts are split
  * into partitions processed in parallel and joined by a log-sum-exp merge.
- * A workspace of
- *   (W + S*Hkv) * G * (d + 1) * 4 + S * Hkv * 8 bytes
- * is allocated and freed stream-ordered on `stream` (hipMallocAsync).
+ * A wavefront that finishes the last partition of a split (sequence, KV
+ * head) pair merges that pair's partitions itself: one kernel per call.
+ *
+ * Workspace: the library keeps one device buffer per (device, stream),
+ * reused by every pa_decode call on that stream and grown when a call needs
+ * more: about (W + S*Hkv) * G * (d + 1) * 4 + S * Hkv * 4 bytes (per-unit
+ * counters, which the kernel leaves at zero, then partial results).  Growing
+ * allocates (hipMallocAsync), zeroes the counters (hipMemsetAsync) and frees
+ * the old buffer (hipFreeAsync), all on `stream`.  Calls on one stream
+ * share the buffer safely; calls on different streams use different
+ * buffers.  Release a stream's buffer with pa_workspace_release before
+ * destroying the stream.
  * Returns PA_OK or a negative pa_status.
  */
 int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
@@ -168,6 +177,14 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
                 const pa_tensor* slot_mapping, const pa_tensor* k_pool,
                 const pa_tensor* v_pool, void* stream);
 
+/*
+ * pa_workspace_release -- frees (stream-ordered, hipFreeAsync) the decode
+ * workspace kept for `stream` on the current device.  Later pa_decode calls
+ * on that stream allocate a new one.  Returns PA_OK (also when the stream
+ * has none) or PA_ERR_LAUNCH.
+ */
+int pa_workspace_release(void* stream);
+
 /* Text for a pa_status value (static storage). */
 const char* pa_status_string(int status);
 
@@ -182,7 +199,7 @@ const char* pa_last_error(void);
  *   waves_per_group   wavefronts per workgroup
  *   grid[3]           workgroups of the partition kernel
  *   block_threads     threads per workgroup
- *   workspace_bytes   stream-ordered workspace
+ *   workspace_bytes   workspace the call needs (counters and partials)
  *
  * The environment variable PA_DECODE_WORKERS (1 .. 2^20) overrides W; the
  * result is the same up to floating-point rounding for every W.
@@ -201,11 +218,12 @@ int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor*
                    const pa_tensor* out, pa_decode_plan_info* info);
 
 /*
- * Kernel timing.  While enabled, every kernel the library launches is
- * bracketed by a pair of HIP events recorded on the launch stream.
+ * Kernel timing.  While enabled, every kernel the library launches carries
+ * a pair of HIP events bound to its dispatch (hipExtLaunchKernelGGL), so the
+ * elapsed time is the kernel's own execution.
  * pa_profiler_read synchronises on the recorded events and adds their
  * elapsed times to per-kernel totals.  Kernel names: "decode_partitions",
- * "decode_merge", "prefill", "write_kv".  Not meant for concurrent use from
+ * "prefill", "write_kv".  Not meant for concurrent use from
  * several threads.
  */
 int pa_profiler_enable(int on);

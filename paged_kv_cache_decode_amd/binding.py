@@ -48,7 +48,8 @@ class PAError(RuntimeError):
 _lib = None
 
 EXPORTS = ("pa_decode", "pa_prefill", "pa_write_kv", "pa_status_string", "pa_last_error",
-           "pa_decode_plan", "pa_profiler_enable", "pa_profiler_reset", "pa_profiler_read")
+           "pa_decode_plan", "pa_workspace_release", "pa_profiler_enable", "pa_profiler_reset",
+           "pa_profiler_read")
 
 
 def lib():
@@ -66,8 +67,9 @@ def lib():
                              P, ctypes.c_void_p]
     L.pa_write_kv.argtypes = [P, P, P, P, P, ctypes.c_void_p]
     L.pa_decode_plan.argtypes = [P, P, P, P, P, P, ctypes.POINTER(PaDecodePlanInfo)]
-    for f in ("pa_decode", "pa_prefill", "pa_write_kv", "pa_decode_plan", "pa_profiler_enable",
-              "pa_profiler_read"):
+    L.pa_workspace_release.argtypes = [ctypes.c_void_p]
+    for f in ("pa_decode", "pa_prefill", "pa_write_kv", "pa_decode_plan", "pa_workspace_release",
+              "pa_profiler_enable", "pa_profiler_read"):
         getattr(L, f).restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
@@ -158,6 +160,11 @@ def write_kv(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
     L = lib()
     args = [describe(x) for x in (k_new, v_new, slot_mapping, k_pool, v_pool)]
     _check(L.pa_write_kv(*[ctypes.byref(a) for a in args], _stream(stream)))
+
+
+def workspace_release(stream=None):
+    """Free the decode workspace the library keeps for `stream`."""
+    _check(lib().pa_workspace_release(_stream(stream)))
 
 
 def profiler_enable(on: bool = True):

@@ -2,6 +2,7 @@
 // kernel launches and error reporting.  See include/pa.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -135,6 +136,56 @@ int decode_workers(const pa_tensor* q, const pa_tensor* k_pool) {
 
 }  // namespace
 
+namespace {
+
+// Decode workspaces, one per (device, stream), kept across calls and grown
+// when a call needs more.  Layout: per-unit counters (zero between calls:
+// the kernel resets every counter it uses) followed by the partial outputs.
+// Calls on one stream run in order, so they can share the buffer; a grown
+// buffer is allocated, its counters zeroed and the old one freed, all
+// stream-ordered on that stream.
+struct StreamWorkspace {
+  void* ptr = nullptr;
+  int64_t counter_bytes = 0;  // capacity of the counter region
+  int64_t part_bytes = 0;     // capacity of the partial-result region
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, void*>, StreamWorkspace> g_ws;
+
+int acquire_workspace(pa::DecodePlan* plan, hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const int64_t need_c = plan->counter_bytes, need_p = plan->ws_bytes - plan->counter_bytes;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  StreamWorkspace& w = g_ws[{dev, static_cast<void*>(stream)}];
+  if (w.ptr == nullptr || w.counter_bytes < need_c || w.part_bytes < need_p) {
+    if (forced_alloc_failure())
+      return set_error(PA_ERR_ALLOC, "workspace of %lld bytes: allocation failure forced by "
+                       "PA_TEST_FAIL_ALLOC", (long long)plan->ws_bytes);
+    const int64_t cb = std::max(w.counter_bytes, need_c);
+    const int64_t pb = std::max(w.part_bytes, need_p + need_p / 4);
+    void* p = nullptr;
+    hipError_t e = hipMallocAsync(&p, (size_t)(cb + pb), stream);
+    if (e != hipSuccess)
+      return set_error(PA_ERR_ALLOC, "hipMallocAsync(%lld bytes): %s", (long long)(cb + pb),
+                       hipGetErrorString(e));
+    e = hipMemsetAsync(p, 0, (size_t)cb, stream);
+    if (e != hipSuccess) {
+      (void)hipFreeAsync(p, stream);
+      return set_error(PA_ERR_LAUNCH, "hipMemsetAsync: %s", hipGetErrorString(e));
+    }
+    if (w.ptr) (void)hipFreeAsync(w.ptr, stream);
+    w.ptr = p;
+    w.counter_bytes = cb;
+    w.part_bytes = pb;
+  }
+  plan->counter_bytes = w.counter_bytes;  // partials start after the counters
+  *out = w.ptr;
+  return PA_OK;
+}
+
+}  // namespace
+
 int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
                    const pa_tensor* block_table, const pa_tensor* context_lens,
                    const pa_tensor* out, pa_decode_plan_info* info) {
@@ -177,18 +228,23 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_po
             plan.workers, (long long)plan.grid[0], (long long)plan.ws_bytes);
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   void* ws = nullptr;
-  {
-    if (forced_alloc_failure())
-      return set_error(PA_ERR_ALLOC, "workspace of %lld bytes: allocation failure forced by "
-                       "PA_TEST_FAIL_ALLOC", (long long)plan.ws_bytes);
-    const hipError_t e = hipMallocAsync(&ws, (size_t)plan.ws_bytes, stream);
-    if (e != hipSuccess)
-      return set_error(PA_ERR_ALLOC, "hipMallocAsync(%lld bytes): %s", (long long)plan.ws_bytes,
-                       hipGetErrorString(e));
-  }
+  st = acquire_workspace(&plan, stream, &ws);
+  if (st) return st;
   const hipError_t e = pa::launch_decode(plan, ws, stream);
-  (void)hipFreeAsync(ws, stream);
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_workspace_release(void* stream_ptr) {
+  g_last_error.clear();
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_ws.find({dev, stream_ptr});
+  if (it == g_ws.end()) return PA_OK;
+  const hipError_t e = hipFreeAsync(it->second.ptr, static_cast<hipStream_t>(stream_ptr));
+  g_ws.erase(it);
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "hipFreeAsync: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

@@ -26,8 +26,10 @@
 // that several sequences share (a common prompt prefix) stay in its L2.
 // The piece of a unit that one worker covers is a partition: a worker that
 // covers a whole unit writes `out` directly; otherwise it writes a
-// normalised partial output and its log2-sum-exp, and the merge kernel
-// joins the partitions of that unit.
+// normalised partial output and its log2-sum-exp and counts itself in the
+// unit's counter, and the worker that completes the count joins the
+// partitions (log-sum-exp merge) and resets the counter to zero for the
+// next call on the stream.  There is no second kernel.
 //
 // Per 16-key tile a worker:
 //   * loads the K rows with the lane layout of the 16x16 MFMA B operand
@@ -76,9 +78,10 @@ struct DecodeArgs {
   void* out;
   int64_t o_ss, o_sh;  // elements
   int out_f32;
-  float* part_o;     // [slots, G, D]
-  float* part_lse;   // [slots, G] (log2 units)
-  int2* unit_range;  // [Hkv * S]: first and last worker of each unit (g-major)
+  float* part_o;    // [slots, G, D]
+  float* part_lse;  // [slots, G] (log2 units)
+  int* counters;    // [Hkv * S] finished partitions per unit (g-major); zero
+                    // between calls
   int S, H, Hkv, W, bs_shift;
   float scale_log2;  // scale * log2(e)
 };
@@ -133,6 +136,83 @@ __device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
 
 __device__ __forceinline__ int tiles_of(int n) { return (n + kTileKeys - 1) / kTileKeys; }
 
+// Partial results cross workgroups (and XCDs, whose L2 caches are not
+// coherent with each other).  They are written and read with relaxed
+// device-scope atomic accesses, which the hardware performs at the coherent
+// level (the sc1 bit) without flushing or invalidating the L2; a writer
+// waits for its stores to complete before it counts its partition.
+__device__ __forceinline__ void store_partial(float* p, float x, float y) {  // p 8-byte aligned
+  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_partial(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int N>
+__device__ __forceinline__ void load_partial(const float* p, float* o) {
+  if constexpr (N == 1) {
+    o[0] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; e += 2) {
+      const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p + e),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      o[e] = __uint_as_float((uint32_t)v);
+      o[e + 1] = __uint_as_float((uint32_t)(v >> 32));
+    }
+  }
+}
+
+// Log-sum-exp merge of the np partitions of unit (g, s), held in slots
+// slot0 .. slot0+np-1, by one wave:
+//   out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),  M = max_p lse_p,
+// computed in one pass with a running maximum.  Lane l owns G*D/64
+// consecutive values of the unit's [G][D] output.
+template <class T, int D, int G>
+__device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, int64_t slot0,
+                                           int np, int lane) {
+  constexpr int kV = G * D / 64;
+  static_assert(kV >= 1 && kV * 64 == G * D, "merge split");
+  const int idx0 = lane * kV;
+  const int h = idx0 / D, d0 = idx0 % D;
+  float M = -INFINITY, wsum = 0.f, acc[kV];
+#pragma unroll
+  for (int e = 0; e < kV; ++e) acc[e] = 0.f;
+  auto add = [&](float lse, const float* o) {
+    const float mn = fmaxf(M, lse);
+    const float sa = fast_exp2(M - mn), sb = fast_exp2(lse - mn);
+    wsum = fmaf(wsum, sa, sb);
+#pragma unroll
+    for (int e = 0; e < kV; ++e) acc[e] = fmaf(acc[e], sa, sb * o[e]);
+    M = mn;
+  };
+  constexpr int kU = 4;  // partitions whose loads are in flight together
+  int p = 0;
+  for (; p + kU <= np; p += kU) {
+    float lse[kU], o[kU][kV];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t slot = slot0 + p + u;
+      load_partial<1>(a.part_lse + slot * G + h, &lse[u]);
+      load_partial<kV>(a.part_o + slot * G * D + idx0, o[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) add(lse[u], o[u]);
+  }
+  for (; p < np; ++p) {
+    const int64_t slot = slot0 + p;
+    float lse, o[kV];
+    load_partial<1>(a.part_lse + slot * G + h, &lse);
+    load_partial<kV>(a.part_o + slot * G * D + idx0, o);
+    add(lse, o);
+  }
+  const float inv = 1.f / wsum;
+  const int64_t ob = (int64_t)s * a.o_ss + (int64_t)(g * G + h) * a.o_sh + d0;
+#pragma unroll
+  for (int e = 0; e < kV; ++e) store_out<T>(a.out, ob + e, acc[e] * inv, a.out_f32 != 0);
+}
+
 template <class T, int D, int G>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(DecodeArgs a) {
   using Geo = DecodeGeom<T, D>;
@@ -147,6 +227,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   const int logical = (blockIdx.x & 7) * (groups >> 3) + (blockIdx.x >> 3);
   const int worker = logical * kNW + w;
   if (worker >= a.W) return;
+
+  // Units with an empty context are in no worker's slice; their output is
+  // zero.  Worker i checks units i, i + W, ...
+  for (int u = worker; u < a.S * a.Hkv; u += a.W) {
+    const int su = u % a.S, gu = u / a.S;
+    if (as_const(a.cl)[su] == 0) {
+      for (int i = lane; i < G * D; i += 64)
+        store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
+                     0.f, a.out_f32 != 0);
+    }
+  }
 
   __shared__ float p_lds[kNW][kTileKeys][4];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kNW][G * Geo::kRowBytes];
@@ -372,120 +463,53 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float inv = 1.f / l_lane[h];
+        if (whole) {
 #pragma unroll
-        for (int e = 0; e < kE; ++e) {
-          const int d = lane * kE + e;
-          if (whole) {
-            store_out<T>(a.out, (int64_t)s * a.o_ss + (int64_t)(hq0 + h) * a.o_sh + d,
+          for (int e = 0; e < kE; ++e)
+            store_out<T>(a.out, (int64_t)s * a.o_ss + (int64_t)(hq0 + h) * a.o_sh + lane * kE + e,
                          acc[h][e] * inv, a.out_f32 != 0);
-          } else {
-            a.part_o[((int64_t)(worker + u) * G + h) * D + d] = acc[h][e] * inv;
-          }
+        } else {
+          float* po = a.part_o + ((int64_t)(worker + u) * G + h) * D + lane * kE;
+#pragma unroll
+          for (int e = 0; e < kE; e += 2)
+            store_partial(po + e, acc[h][e] * inv, acc[h][e + 1] * inv);
         }
       }
     }
-    if (lane == 0) {
-      if (!whole) {
+    if (!whole) {
+      if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
-          a.part_lse[(int64_t)(worker + u) * G + h] = m[h] + __log2f(l_lane[h]);
+          store_partial(a.part_lse + (int64_t)(worker + u) * G + h, m[h] + __log2f(l_lane[h]));
       }
-      if (j0 == 0) {
-        // First worker of the unit records which workers hold its pieces.
-        const int last = (int)((unit_first + ts - 1) / per);
-        a.unit_range[u] = make_int2(worker, last);
+      // Workers first .. last hold the unit's partitions (slots worker + u).
+      const int first = (int)(unit_first / per);
+      const int last = (int)((unit_first + ts - 1) / per);
+      // Once this wave's partial stores have completed, count the partition;
+      // the worker that brings the count to the number of partitions merges
+      // them and leaves the counter at zero.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      int done = 0;
+      if (lane == 0) done = __hip_atomic_fetch_add(a.counters + u, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      done = __builtin_amdgcn_readfirstlane(done);
+      if (done == last - first) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        merge_unit<T, D, G>(a, g, s, (int64_t)first + u, last - first + 1, lane);
+        if (lane == 0)
+          __hip_atomic_store(a.counters + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     t = unit_first + j1;
   }
 }
 
-// Joins the partitions of units split over several workers:
-// out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),  M = max_p lse_p.
-// Also writes the zero output of empty contexts.  One 256-thread workgroup
-// per (sequence, query head): every thread accumulates 4 output columns
-// over a strided subset of the partitions with independent 16-byte loads.
-constexpr int kMergeThreads = 256;
-
-template <class T, int D, int G>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int kChunks = D / 4;                    // 16-byte column chunks of a row
-  constexpr int kGroups = kMergeThreads / kChunks;  // partition subsets
-  const int hq = blockIdx.x, s = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int n = a.cl[s];
-  const int g = hq / G, h = hq % G;
-  const int64_t ob = (int64_t)s * a.o_ss + (int64_t)hq * a.o_sh;
-  if (n == 0) {
-    for (int d = tid; d < D; d += kMergeThreads) store_out<T>(a.out, ob + d, 0.f, a.out_f32 != 0);
-    return;
-  }
-  const int u = g * a.S + s;
-  const int2 range = a.unit_range[u];
-  const int np = range.y - range.x + 1;
-  if (np <= 1) return;  // the single worker wrote `out` itself
-  const int64_t slot0 = (int64_t)range.x + u;
-
-  __shared__ float red[kMergeThreads / 64];
-  __shared__ float wts[kMergeThreads];
-  __shared__ f32x4_t part[kGroups][kChunks];
-
-  float M = -INFINITY;
-  for (int p = tid; p < np; p += kMergeThreads) M = fmaxf(M, a.part_lse[(slot0 + p) * G + h]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i]);
-
-  const int cidx = tid % kChunks, pg = tid / kChunks;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  for (int p0 = 0; p0 < np; p0 += kMergeThreads) {
-    const int cnt = min(kMergeThreads, np - p0);
-    __syncthreads();
-    if (tid < cnt) {
-      const float wv = fast_exp2(a.part_lse[(slot0 + p0 + tid) * G + h] - M);
-      wts[tid] = wv;
-      wsum += wv;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int j = pg; j < cnt; j += kGroups) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(
-          a.part_o + ((slot0 + p0 + j) * G + h) * D + cidx * 4);
-      acc += wts[j] * v;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o);
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = wsum;
-  part[pg][cidx] = acc;
-  __syncthreads();
-  float W = red[0];
-#pragma unroll
-  for (int i = 1; i < kMergeThreads / 64; ++i) W += red[i];
-  if (tid < kChunks) {
-    f32x4_t o = part[0][tid];
-#pragma unroll
-    for (int g2 = 1; g2 < kGroups; ++g2) o += part[g2][tid];
-    const float inv = 1.f / W;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) store_out<T>(a.out, ob + tid * 4 + e, o[e] * inv, a.out_f32 != 0);
-  }
-}
-
 template <class T, int D, int G>
 hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t stream) {
-  const hipError_t e =
-      timed_launch("decode_partitions", decode_partitions_kernel<T, D, G>,
-                   dim3((unsigned)pl.grid[0]), dim3(pl.block_threads), stream, a);
-  if (e != hipSuccess) return e;
-  return timed_launch("decode_merge", decode_merge_kernel<T, D, G>, dim3(pl.H, pl.S),
-                      dim3(kMergeThreads), stream, a);
+  return timed_launch("decode_partitions", decode_partitions_kernel<T, D, G>,
+                      dim3((unsigned)pl.grid[0]), dim3(pl.block_threads), stream, a);
 }
 
 template <class T, int D, int G>
@@ -572,9 +596,10 @@ hipError_t launch_decode(const DecodePlan& pl, void* workspace, hipStream_t stre
   a.o_ss = pl.o_ss;
   a.o_sh = pl.o_sh;
   a.out_f32 = pl.out_dtype == PA_F32;
-  a.part_o = static_cast<float*>(workspace);
+  // Workspace: counters [S*Hkv] int32 (padded to 256 bytes) | part_o | part_lse.
+  a.counters = static_cast<int*>(workspace);
+  a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + pl.counter_bytes);
   a.part_lse = a.part_o + pl.slots * pl.G * pl.D;
-  a.unit_range = reinterpret_cast<int2*>(a.part_lse + pl.slots * pl.G);
   a.S = pl.S;
   a.H = pl.H;
   a.Hkv = pl.Hkv;

@@ -224,8 +224,10 @@ int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_
   p.grid[0] = ((workers + kDecodeWaves - 1) / kDecodeWaves + 7) / 8 * 8;
   p.grid[1] = 1;
   p.grid[2] = 1;
-  // part_o [slots, G, D] f32 | part_lse [slots, G] f32 | unit ranges [S*Hkv] int2
-  p.ws_bytes = p.slots * G * D * 4 + p.slots * G * 4 + S * Hkv * 8;
+  // counters [S*Hkv] int32, padded to 256 B | part_o [slots, G, D] f32 |
+  // part_lse [slots, G] f32
+  p.counter_bytes = ((int64_t)S * Hkv * 4 + 255) / 256 * 256;
+  p.ws_bytes = p.counter_bytes + p.slots * G * D * 4 + p.slots * G * 4;
   p.q = q->data; p.q_ss = q->stride[0]; p.q_sh = q->stride[1];
   p.k = k_pool->data; p.v = v_pool->data;
   p.bt = static_cast<const int32_t*>(block_table->data); p.bt_ss = block_table->stride[0];

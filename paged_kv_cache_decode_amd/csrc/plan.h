@@ -16,7 +16,7 @@ namespace pa {
 // wavefront each, kDecodeWaves per workgroup); all (sequence, KV head)
 // units' 16-key tiles form one list that is cut into equal contiguous
 // slices, one per worker.  A worker's piece of one unit is a partition;
-// units split over several workers are joined by the merge kernel.
+// the last worker to finish a split unit joins its partitions.
 constexpr int kDecodeWaves = 4;
 constexpr int kTileKeys = 16;
 constexpr int kMaxWorkers = 1 << 20;
@@ -30,7 +30,8 @@ struct DecodePlan {
   int64_t slots = 0;     // partial-result slots: workers + S * Hkv
   int64_t grid[3] = {0, 0, 0};
   int block_threads = 0;
-  int64_t ws_bytes = 0;  // partial outputs, log-sum-exp and per-unit ranges
+  int64_t counter_bytes = 0;  // per-unit counters at the start of the workspace
+  int64_t ws_bytes = 0;       // counters, partial outputs and log-sum-exp
   // operands
   const void* q = nullptr;
   int64_t q_ss = 0, q_sh = 0;  // strides (elements) over sequence and head

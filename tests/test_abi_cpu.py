@@ -136,7 +136,8 @@ def test_decode_plan_math(monkeypatch):
     assert tuple(info.grid) == (-(-W // 32) * 8, 1, 1)  # groups, a multiple of 8
     G, d, S, Hkv = 4, 128, 64, 8
     slots = W + S * Hkv
-    assert info.workspace_bytes == slots * G * d * 4 + slots * G * 4 + S * Hkv * 8
+    counters = -(-S * Hkv * 4 // 256) * 256  # per-unit counters, padded to 256 bytes
+    assert info.workspace_bytes == counters + slots * G * d * 4 + slots * G * 4
     # A long-context shape: 4 x 100,000 keys (6,250 blocks of 16); 64-bit sizes.
     st, info = plan(decode_args(S=4, MB=6250, NB=31250))
     assert st == 0

@@ -96,6 +96,36 @@ def test_decode_is_deterministic(pa):
     assert torch.equal(a, b)
 
 
+def test_decode_workspace_reuse_across_calls_and_streams(pa, monkeypatch):
+    """The per-unit counters of the kept workspace return to zero after every
+    call: alternating shapes (more units, then fewer, then a split of every
+    unit over many workers) on one stream and on a second stream reproduce
+    each shape's first result bit for bit, and match the oracle."""
+    monkeypatch.setenv("PA_DECODE_WORKERS", "512")
+    small = W.make_decode_case(303, 3, 8, 2, 128, 16, "f16", lens=[900, 4000, 17],
+                               max_blocks=256)
+    big = W.make_decode_case(304, 24, 32, 8, 128, 16, "f16", len_range=(1, 4096),
+                             max_blocks=256)
+    cases = [(small, case_to_dev(small)), (big, case_to_dev(big))]
+    refs = [oracle_decode(c) for c, _ in cases]
+    first = [run_decode(pa, c, dev=d) for c, d in cases]
+    for (c, _), got, ref in zip(cases, first, refs):
+        assert_close_f32_out(out_to_f64(got), ref, "f16", "workspace reuse")
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        for i in (1, 0):
+            c, d = cases[i]
+            assert torch.equal(run_decode(pa, c, dev=d), first[i]), (rep, i)
+            with torch.cuda.stream(side):
+                out = pa.decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"],
+                                d["context_lens"], c.scale, out_dtype=torch.float32,
+                                stream=side.cuda_stream)
+            side.synchronize()
+            assert torch.equal(out, first[i]), ("side stream", rep, i)
+    pa.workspace_release(side.cuda_stream)
+    side.synchronize()
+
+
 def test_decode_placement_invariance_bit_exact(pa):
     """Same logical K/V, two different physical placements: identical bits."""
     base = W.make_decode_case(302, 4, 8, 2, 128, 16, "bf16", lens=[33, 300, 1000, 2500],
