@@ -16,7 +16,7 @@
 // (sequence s, KV head g) pair with the G query heads that share g; it has
 // ceil(n_s / 16) tiles of 16 keys.  The tiles of all units, KV-head major
 // ((g, s) order), form one list of `total` tiles.  The kernel launches W
-// wavefronts ("workers", as many as the device keeps resident) and gives
+// wavefronts ("workers", one workgroup of four per compute unit) and gives
 // worker i the contiguous slice [i*q, (i+1)*q) of the list,
 // q = ceil(total / W), so every worker streams the same number of bytes
 // whatever the mix of context lengths -- no tail of long partitions, no idle
@@ -54,6 +54,11 @@
 
 namespace pa {
 namespace {
+
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 3
+#endif
+constexpr int kDecodeDepth = PA_DECODE_DEPTH;
 
 template <class T, int D>
 struct DecodeGeom {
@@ -216,6 +221,7 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, in
 template <class T, int D, int G>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(DecodeArgs a) {
   using Geo = DecodeGeom<T, D>;
+  constexpr int kDepth = kDecodeDepth;  // tiles whose loads are in flight per wave
   constexpr int kNW = kDecodeWaves;
   constexpr int kE = Geo::kE;
 
@@ -344,9 +350,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
       for (int e = 0; e < kE; ++e) acc[h][e] = 0.f;
     }
 
-    u32x4_t kA[Geo::kKLoads], vA[Geo::kVLoads];
-    u32x4_t kB[Geo::kKLoads], vB[Geo::kVLoads];
-    u32x4_t kC[Geo::kKLoads], vC[Geo::kVLoads];
+    u32x4_t kr[kDepth][Geo::kKLoads], vr[kDepth][Geo::kVLoads];
 
     auto load_tile = [&](int k, u32x4_t* kd, u32x4_t* vd) {
       const int key0 = uniform_i((j0 + min(k, ntile - 1)) * kTileKeys);
@@ -356,9 +360,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
       const uint8_t* vb = vbase + row0;
 #pragma unroll
       for (int i = 0; i < Geo::kKLoads; ++i) kd[i] = load16(kb + k_off + i * 64);
+      // V rows are read whole by one instruction each: non-temporal, so
+      // streaming V does not push reusable lines out of the caches.  K rows
+      // are read 64 bytes at a time by four instructions, and the second
+      // half of each 128-byte line must still be in L2 when it is needed.
 #pragma unroll
       for (int i = 0; i < Geo::kVLoads; ++i)
-        vd[i] = load16(vb + (int64_t)(i * Geo::kRPI) * tok_stride + v_off);
+        vd[i] = load16_stream(vb + (int64_t)(i * Geo::kRPI) * tok_stride + v_off);
     };
 
     auto compute_tile = [&](int k, const u32x4_t* kf, const u32x4_t* vf) {
@@ -418,33 +426,33 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
       __builtin_amdgcn_wave_barrier();
     };
 
-    // Three-way rotation over this partition's tiles: the steady-state loop
+    // kDepth-way rotation over this partition's tiles: the steady-state loop
     // issues one tile's loads per computed tile (fixed waits); an epilogue
-    // finishes the last one to five tiles without loading past the end.
-    load_tile(0, kA, vA);
-    load_tile(1, kB, vB);  // the first loads are clamped to the last tile
-    load_tile(2, kC, vC);  // of a partition shorter than three tiles
+    // finishes the last 1 .. 2*kDepth-1 tiles without loading past the end.
+    // The first loads are clamped to the last tile of a short partition.
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) load_tile(i, kr[i], vr[i]);
 #pragma unroll
     for (int j = 0; j < kQPer; ++j)
       if (lane + 64 * j < kQChunks) *reinterpret_cast<u32x4_t*>(my_q + (lane + 64 * j) * 16) = qreg[j];
     __builtin_amdgcn_wave_barrier();
     int k = 0;
-    for (; k + 5 < ntile; k += 3) {
-      compute_tile(k, kA, vA);
-      load_tile(k + 3, kA, vA);
-      compute_tile(k + 1, kB, vB);
-      load_tile(k + 4, kB, vB);
-      compute_tile(k + 2, kC, vC);
-      load_tile(k + 5, kC, vC);
+    for (; k + 2 * kDepth - 1 < ntile; k += kDepth) {
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) {
+        compute_tile(k + i, kr[i], vr[i]);
+        load_tile(k + kDepth + i, kr[i], vr[i]);
+      }
     }
-    const int rest = ntile - k;  // 1..5; A, B, C hold tiles k, k + 1, k + 2
-    compute_tile(k, kA, vA);
-    if (rest > 3) load_tile(k + 3, kA, vA);
-    if (rest > 1) compute_tile(k + 1, kB, vB);
-    if (rest > 4) load_tile(k + 4, kB, vB);
-    if (rest > 2) compute_tile(k + 2, kC, vC);
-    if (rest > 3) compute_tile(k + 3, kA, vA);
-    if (rest > 4) compute_tile(k + 4, kB, vB);
+    const int rest = ntile - k;  // 1 .. 2*kDepth-1; set i holds tile k + i
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      if (i < rest) compute_tile(k + i, kr[i], vr[i]);
+      if (kDepth + i < rest) load_tile(k + kDepth + i, kr[i], vr[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i)
+      if (kDepth + i < rest) compute_tile(k + kDepth + i, kr[i], vr[i]);
 
     // Partition totals: l over the 16 keys of a row, acc over lanes sharing
     // a column.
@@ -512,6 +520,10 @@ hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
                       dim3((unsigned)pl.grid[0]), dim3(pl.block_threads), stream, a);
 }
 
+// One workgroup (kDecodeWaves wavefronts) per compute unit.  Measured on
+// MI355X, one wavefront per SIMD with three tiles in flight streams K/V
+// faster than two: fewer, longer slices mean fewer pipeline restarts at unit
+// boundaries and fewer partitions, with enough bytes still in flight.
 template <class T, int D, int G>
 int resident_waves_t() {
   int dev = 0, cus = 0, per_cu = 0;
@@ -522,7 +534,7 @@ int resident_waves_t() {
           &per_cu, reinterpret_cast<const void*>(decode_partitions_kernel<T, D, G>),
           64 * kDecodeWaves, 0) != hipSuccess)
     return 0;
-  return cus * per_cu * kDecodeWaves;
+  return per_cu >= 1 ? cus * kDecodeWaves : 0;
 }
 
 template <class T>
@@ -574,8 +586,8 @@ int decode_worker_count(int dtype, int D, int G) {
       default: break;
     }
   }
-  // Without a device (planning only) assume an MI355X: 256 CUs x 12 waves.
-  if (w <= 0) w = 256 * 12;
+  // Without a device (planning only) assume an MI355X: 256 CUs.
+  if (w <= 0) w = 256 * kDecodeWaves;
   std::lock_guard<std::mutex> lk(mu);
   cache[key] = w;
   return w;

@@ -12,8 +12,9 @@ namespace pa {
 // holds plan.ws_bytes bytes.
 hipError_t launch_decode(const DecodePlan& plan, void* workspace, hipStream_t stream);
 
-// Wavefronts of the decode kernel the current device keeps resident for
-// this instance (falls back to an MI355X's 256 CUs x 12 without a device).
+// Decode workers for this instance on the current device: one workgroup of
+// kDecodeWaves wavefronts per compute unit (an MI355X's 256 CUs without a
+// device).
 int decode_worker_count(int dtype, int D, int G);
 
 hipError_t launch_prefill(const PrefillPlan& plan, hipStream_t stream);
