@@ -218,6 +218,21 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, in
   for (int e = 0; e < kV; ++e) store_out<T>(a.out, ob + e, acc[e] * inv, a.out_f32 != 0);
 }
 
+// Units with an empty context are in no worker's slice; their output is
+// zero.  Worker i writes units i, i + W, ... (after its own slice, so that
+// the check is off the path to the first K/V loads).
+template <class T, int D, int G>
+__device__ __forceinline__ void zero_empty_units(const DecodeArgs& a, int worker, int lane) {
+  for (int u = worker; u < a.S * a.Hkv; u += a.W) {
+    const int su = u % a.S, gu = u / a.S;
+    if (as_const(a.cl)[su] == 0) {
+      for (int i = lane; i < G * D; i += 64)
+        store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
+                     0.f, a.out_f32 != 0);
+    }
+  }
+}
+
 template <class T, int D, int G>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(DecodeArgs a) {
   using Geo = DecodeGeom<T, D>;
@@ -234,24 +249,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   const int worker = logical * kNW + w;
   if (worker >= a.W) return;
 
-  // Units with an empty context are in no worker's slice; their output is
-  // zero.  Worker i checks units i, i + W, ...
-  for (int u = worker; u < a.S * a.Hkv; u += a.W) {
-    const int su = u % a.S, gu = u / a.S;
-    if (as_const(a.cl)[su] == 0) {
-      for (int i = lane; i < G * D; i += 64)
-        store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
-                     0.f, a.out_f32 != 0);
-    }
-  }
-
   __shared__ float p_lds[kNW][kTileKeys][4];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kNW][G * Geo::kRowBytes];
 
   // ---- this worker's slice of the global tile list ----
   // Tiles per KV head over all sequences (the list is g-major).  With at
   // most 64 sequences one load of the lengths serves both passes.
-  const int lane_tiles = lane < a.S ? tiles_of(as_const(a.cl)[lane]) : 0;
+  const int lane_len = lane < a.S ? as_const(a.cl)[lane] : 0;
+  const int lane_tiles = tiles_of(lane_len);
   int64_t t_all = wave_sum_i64(lane_tiles);
   for (int c0 = 64; c0 < a.S; c0 += 64) {
     const int s = c0 + lane;
@@ -261,7 +266,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   const int64_t per = (total + a.W - 1) / a.W;
   const int64_t begin = (int64_t)worker * per;
   const int64_t end = min(total, begin + per);
-  if (begin >= end) return;
+  if (begin >= end) {
+    zero_empty_units<T, D, G>(a, worker, lane);
+    return;
+  }
 
   // KV head and sequence holding `begin`, and the list index of the first
   // tile of that sequence's unit.
@@ -307,7 +315,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     // table and length reads below become scalar loads.)
     s = uniform_i(s);
     g = uniform_i(g);
-    const int n = as_const(a.cl)[s];
+    // With at most 64 sequences every length is already in a register.
+    const int n = a.S <= 64 ? __builtin_amdgcn_readlane(lane_len, s) : as_const(a.cl)[s];
     const int ts = tiles_of(n);
     if (t >= unit_first + ts) {  // empty or finished unit: next sequence / head
       unit_first += ts;
@@ -512,6 +521,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     }
     t = unit_first + j1;
   }
+  zero_empty_units<T, D, G>(a, worker, lane);
 }
 
 template <class T, int D, int G>
