@@ -178,6 +178,68 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
                 const pa_tensor* v_pool, void* stream);
 
 /*
+ * pa_copy_blocks -- copy whole physical blocks src[i] -> dst[i] in both
+ * pools (the copy-on-write step of "FlashAttention and PagedAttention: two
+ * fixes for two different bottlenecks", "PagedAttention - How it works":
+ * a block shared by several sequences is duplicated before one of them
+ * writes to it).
+ *
+ *   k_pool, v_pool   [NB, B, Hkv, d]  written in place
+ *   src, dst         int32 [N] device arrays of block ids in [0, NB); no dst
+ *                    may equal any src or another dst (device contents:
+ *                    contract)
+ */
+int pa_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_tensor* src,
+                   const pa_tensor* dst, void* stream);
+
+/*
+ * Host block manager: the logical-to-physical block tables the kernels
+ * read, following the block-table management of "Flash Attention vs Paged
+ * Attention" (blocks handed out on demand from a free list, returned when
+ * no sequence holds them) and the sharing of "FlashAttention and
+ * PagedAttention: two fixes for two different bottlenecks", "PagedAttention
+ * - How it works" (a forked sequence shares its parent's blocks; a shared
+ * block is copied when one of its sequences writes into it).  Host memory
+ * only; every call is serialised by a lock inside the manager.  Functions
+ * returning int return PA_OK (or a count) or a negative pa_status with
+ * pa_last_error() set.
+ *
+ * pa_bm_create(num_blocks, block_size)  -- NULL on invalid sizes or no memory
+ * pa_bm_destroy(bm)
+ * pa_bm_num_free(bm)                    -- free blocks
+ * pa_bm_refcount(bm, block)             -- sequences holding `block`
+ * pa_bm_add(bm, seq_id)                 -- new empty sequence (id >= 0)
+ * pa_bm_fork(bm, parent, child)         -- child shares all of parent's
+ *                                          blocks and tokens
+ * pa_bm_append(bm, seq_id, n, slots_out)
+ *     adds n tokens; slots_out[i] = block * B + position of the i-th new
+ *     token (the slot_mapping of pa_write_kv).  Blocks are taken on demand.
+ *     If the sequence's last, partly filled block is shared, it is first
+ *     replaced by a fresh block and the pair (old, fresh) is queued: the
+ *     caller copies it (pa_copy_blocks) before writing the new tokens.
+ *     PA_ERR_ALLOC when too few blocks are free; the sequence is unchanged.
+ * pa_bm_take_copies(bm, src, dst, max)  -- moves up to max queued pairs out,
+ *                                          returns how many
+ * pa_bm_free(bm, seq_id)                -- releases the sequence
+ * pa_bm_block_table(bm, seq_ids, S, MB, table, lens)
+ *     host int32 table[S * MB] (row s: the blocks of seq_ids[s], then -1)
+ *     and lens[S] (tokens), ready to copy to the device for pa_decode /
+ *     pa_prefill.  PA_ERR_SHAPE if a sequence holds more than MB blocks.
+ */
+typedef struct pa_block_manager pa_block_manager;
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+int32_t pa_bm_num_free(pa_block_manager* bm);
+int32_t pa_bm_refcount(pa_block_manager* bm, int32_t block);
+int pa_bm_add(pa_block_manager* bm, int64_t seq_id);
+int pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int32_t n, int32_t* slots_out);
+int pa_bm_take_copies(pa_block_manager* bm, int32_t* src, int32_t* dst, int32_t max);
+int pa_bm_free(pa_block_manager* bm, int64_t seq_id);
+int pa_bm_block_table(pa_block_manager* bm, const int64_t* seq_ids, int32_t S, int32_t MB,
+                      int32_t* table, int32_t* lens);
+
+/*
  * pa_workspace_release -- frees (stream-ordered, hipFreeAsync) the decode
  * workspace kept for `stream` on the current device.  Later pa_decode calls
  * on that stream allocate a new one.  Returns PA_OK (also when the stream
@@ -223,7 +285,7 @@ int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor*
  * elapsed time is the kernel's own execution.
  * pa_profiler_read synchronises on the recorded events and adds their
  * elapsed times to per-kernel totals.  Kernel names: "decode_partitions",
- * "prefill", "write_kv".  Not meant for concurrent use from
+ * "prefill", "write_kv", "copy_blocks".  Not meant for concurrent use from
  * several threads.
  */
 int pa_profiler_enable(int on);

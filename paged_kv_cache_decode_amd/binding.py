@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -47,9 +48,11 @@ class PAError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ("pa_decode", "pa_prefill", "pa_write_kv", "pa_status_string", "pa_last_error",
-           "pa_decode_plan", "pa_workspace_release", "pa_profiler_enable", "pa_profiler_reset",
-           "pa_profiler_read")
+EXPORTS = ("pa_decode", "pa_prefill", "pa_write_kv", "pa_copy_blocks", "pa_status_string",
+           "pa_last_error", "pa_decode_plan", "pa_workspace_release", "pa_profiler_enable",
+           "pa_profiler_reset", "pa_profiler_read", "pa_bm_create", "pa_bm_destroy",
+           "pa_bm_num_free", "pa_bm_refcount", "pa_bm_add", "pa_bm_fork", "pa_bm_append",
+           "pa_bm_take_copies", "pa_bm_free", "pa_bm_block_table")
 
 
 def lib():
@@ -68,8 +71,24 @@ def lib():
     L.pa_write_kv.argtypes = [P, P, P, P, P, ctypes.c_void_p]
     L.pa_decode_plan.argtypes = [P, P, P, P, P, P, ctypes.POINTER(PaDecodePlanInfo)]
     L.pa_workspace_release.argtypes = [ctypes.c_void_p]
-    for f in ("pa_decode", "pa_prefill", "pa_write_kv", "pa_decode_plan", "pa_workspace_release",
-              "pa_profiler_enable", "pa_profiler_read"):
+    L.pa_copy_blocks.argtypes = [P, P, P, P, ctypes.c_void_p]
+    V, I32P, I64P = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    L.pa_bm_create.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    L.pa_bm_create.restype = V
+    L.pa_bm_destroy.argtypes = [V]
+    L.pa_bm_destroy.restype = None
+    L.pa_bm_num_free.argtypes = [V]
+    L.pa_bm_refcount.argtypes = [V, ctypes.c_int32]
+    L.pa_bm_add.argtypes = [V, ctypes.c_int64]
+    L.pa_bm_fork.argtypes = [V, ctypes.c_int64, ctypes.c_int64]
+    L.pa_bm_append.argtypes = [V, ctypes.c_int64, ctypes.c_int32, I32P]
+    L.pa_bm_take_copies.argtypes = [V, I32P, I32P, ctypes.c_int32]
+    L.pa_bm_free.argtypes = [V, ctypes.c_int64]
+    L.pa_bm_block_table.argtypes = [V, I64P, ctypes.c_int32, ctypes.c_int32, I32P, I32P]
+    for f in ("pa_decode", "pa_prefill", "pa_write_kv", "pa_copy_blocks", "pa_decode_plan",
+              "pa_workspace_release", "pa_profiler_enable", "pa_profiler_read", "pa_bm_num_free",
+              "pa_bm_refcount", "pa_bm_add", "pa_bm_fork", "pa_bm_append", "pa_bm_take_copies",
+              "pa_bm_free", "pa_bm_block_table"):
         getattr(L, f).restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
@@ -160,6 +179,82 @@ def write_kv(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
     L = lib()
     args = [describe(x) for x in (k_new, v_new, slot_mapping, k_pool, v_pool)]
     _check(L.pa_write_kv(*[ctypes.byref(a) for a in args], _stream(stream)))
+
+
+def copy_blocks(k_pool, v_pool, src, dst, stream=None):
+    """Copy whole blocks src[i] -> dst[i] in both pools (device int32 ids)."""
+    L = lib()
+    args = [describe(x) for x in (k_pool, v_pool, src, dst)]
+    _check(L.pa_copy_blocks(*[ctypes.byref(a) for a in args], _stream(stream)))
+
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class BlockManager:
+    """The library's host block manager (``pa_bm_*``): block tables, on-demand
+    blocks, forks that share blocks, copy-on-write pairs."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._L = lib()
+        self._h = self._L.pa_bm_create(num_blocks, block_size)
+        if not self._h:
+            raise PAError(-8, self._L.pa_last_error().decode())
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            self._L.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _call(self, st):
+        if st < 0:
+            raise PAError(st, self._L.pa_last_error().decode())
+        return st
+
+    @property
+    def num_free(self) -> int:
+        return self._call(self._L.pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return self._call(self._L.pa_bm_refcount(self._h, block))
+
+    def add(self, seq_id: int):
+        self._call(self._L.pa_bm_add(self._h, seq_id))
+
+    def fork(self, parent: int, child: int):
+        self._call(self._L.pa_bm_fork(self._h, parent, child))
+
+    def append(self, seq_id: int, n: int) -> np.ndarray:
+        """Slots (block * B + position) of n new tokens, int32 [n]."""
+        out = np.empty(max(n, 1), dtype=np.int32)
+        self._call(self._L.pa_bm_append(self._h, seq_id, n, _i32p(out)))
+        return out[:n]
+
+    def take_copies(self, max_pairs: int = 1 << 16):
+        """Queued copy-on-write pairs as (src, dst) int32 arrays."""
+        src = np.empty(max_pairs, dtype=np.int32)
+        dst = np.empty(max_pairs, dtype=np.int32)
+        k = self._call(self._L.pa_bm_take_copies(self._h, _i32p(src), _i32p(dst), max_pairs))
+        return src[:k].copy(), dst[:k].copy()
+
+    def free(self, seq_id: int):
+        self._call(self._L.pa_bm_free(self._h, seq_id))
+
+    def block_table(self, seq_ids, max_blocks: int):
+        """(table int32 [S, max_blocks] with -1 padding, lens int32 [S])."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        S = len(ids)
+        table = np.empty((max(S, 1), max(max_blocks, 1)), dtype=np.int32)
+        lens = np.empty(max(S, 1), dtype=np.int32)
+        self._call(self._L.pa_bm_block_table(
+            self._h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), S, max_blocks,
+            _i32p(table), _i32p(lens)))
+        return table[:S, :max_blocks].copy(), lens[:S].copy()
 
 
 def workspace_release(stream=None):

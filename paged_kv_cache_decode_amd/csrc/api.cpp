@@ -77,6 +77,8 @@ void drain_pending_locked() {
 
 namespace pa {
 
+void set_last_error(const char* msg) { g_last_error = msg; }
+
 bool profiler_enabled() { return g_prof_on; }
 
 KernelTimer::KernelTimer(const char* name) : name_(name) {
@@ -278,6 +280,18 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new, const pa_tensor*
   const hipError_t e = pa::launch_write_kv(plan, static_cast<hipStream_t>(stream_ptr));
   if (e != hipSuccess)
     return set_error(PA_ERR_LAUNCH, "write_kv launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_tensor* src,
+                   const pa_tensor* dst, void* stream_ptr) {
+  g_last_error.clear();
+  pa::CopyBlocksPlan plan;
+  const int st = pa::plan_copy_blocks(k_pool, v_pool, src, dst, &plan, &g_last_error);
+  if (st) return st;
+  const hipError_t e = pa::launch_copy_blocks(plan, static_cast<hipStream_t>(stream_ptr));
+  if (e != hipSuccess)
+    return set_error(PA_ERR_LAUNCH, "copy_blocks launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

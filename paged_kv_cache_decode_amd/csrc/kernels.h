@@ -21,6 +21,8 @@ hipError_t launch_prefill(const PrefillPlan& plan, hipStream_t stream);
 
 hipError_t launch_write_kv(const WriteKvPlan& plan, hipStream_t stream);
 
+hipError_t launch_copy_blocks(const CopyBlocksPlan& plan, hipStream_t stream);
+
 // Kernel timer.  While the profiler is enabled, a KernelTimer holds a pair
 // of events that timed_launch (launch.h) binds to one kernel dispatch; the
 // pair is queued for reading by commit() and released otherwise.

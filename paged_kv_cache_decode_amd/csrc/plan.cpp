@@ -363,4 +363,31 @@ int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
   return PA_OK;
 }
 
+int plan_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_tensor* src,
+                     const pa_tensor* dst, CopyBlocksPlan* plan, std::string* err) {
+  int st;
+  if ((st = check_pools(k_pool, v_pool, err))) return st;
+  if ((st = check_i32(src, "src", 1, err))) return st;
+  if ((st = check_i32(dst, "dst", 1, err))) return st;
+  if (!is_float(k_pool->dtype)) return fail(err, PA_ERR_DTYPE, "pools must be f32/f16/bf16");
+  if (src->shape[0] != dst->shape[0])
+    return fail(err, PA_ERR_SHAPE, "src has %lld entries, dst %lld", (long long)src->shape[0],
+                (long long)dst->shape[0]);
+  const int64_t block_bytes =
+      k_pool->shape[1] * k_pool->shape[2] * k_pool->shape[3] * elem_bytes(k_pool->dtype);
+  if (block_bytes % 16)
+    return fail(err, PA_ERR_UNSUPPORTED, "a block must be a multiple of 16 bytes");
+  if (src->shape[0] * (block_bytes / 16) > ((int64_t)1 << 38))
+    return fail(err, PA_ERR_UNSUPPORTED, "copy too large");
+  CopyBlocksPlan p;
+  p.N = src->shape[0];
+  p.block_bytes = block_bytes;
+  p.src = static_cast<const int32_t*>(src->data);
+  p.dst = static_cast<const int32_t*>(dst->data);
+  p.kp = k_pool->data;
+  p.vp = v_pool->data;
+  *plan = p;
+  return PA_OK;
+}
+
 }  // namespace pa

@@ -84,6 +84,15 @@ struct WriteKvPlan {
   void* vp = nullptr;
 };
 
+struct CopyBlocksPlan {
+  int64_t N = 0;           // block pairs
+  int64_t block_bytes = 0; // bytes of one block in one pool
+  const int32_t* src = nullptr;
+  const int32_t* dst = nullptr;
+  void* kp = nullptr;
+  void* vp = nullptr;
+};
+
 // Validates the decode arguments and sizes the launch for `workers`
 // wavefronts (the device's resident capacity, or an override).
 int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
@@ -98,6 +107,9 @@ int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v
 int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
                   const pa_tensor* slot_mapping, const pa_tensor* k_pool,
                   const pa_tensor* v_pool, WriteKvPlan* plan, std::string* err);
+
+int plan_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_tensor* src,
+                     const pa_tensor* dst, CopyBlocksPlan* plan, std::string* err);
 
 // Reads PA_DECODE_WORKERS (1 .. kMaxWorkers); 0 when unset, -1 when invalid.
 int workers_override_from_env();

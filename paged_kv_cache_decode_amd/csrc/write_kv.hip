@@ -63,4 +63,42 @@ hipError_t launch_write_kv(const WriteKvPlan& pl, hipStream_t stream) {
                       dim3(256), stream, a);
 }
 
+namespace {
+
+struct CopyBlocksArgs {
+  const int32_t* src;
+  const int32_t* dst;
+  uint8_t* kp;
+  uint8_t* vp;
+  int64_t chunks;  // 16-byte pieces per block
+  int64_t total;   // pairs * chunks
+};
+
+// Copy-on-write: whole physical blocks src[i] -> dst[i] in both pools, one
+// thread per 16-byte piece of K and the same piece of V.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.total) return;
+  const int64_t i = idx / a.chunks, c = idx % a.chunks;
+  const int64_t bytes = a.chunks * 16;
+  const int64_t from = (int64_t)a.src[i] * bytes + c * 16, to = (int64_t)a.dst[i] * bytes + c * 16;
+  *reinterpret_cast<u32x4_t*>(a.kp + to) = load16(a.kp + from);
+  *reinterpret_cast<u32x4_t*>(a.vp + to) = load16(a.vp + from);
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksPlan& pl, hipStream_t stream) {
+  CopyBlocksArgs a;
+  a.src = pl.src;
+  a.dst = pl.dst;
+  a.kp = static_cast<uint8_t*>(pl.kp);
+  a.vp = static_cast<uint8_t*>(pl.vp);
+  a.chunks = pl.block_bytes / 16;
+  a.total = pl.N * a.chunks;
+  if (a.total == 0) return hipSuccess;
+  return timed_launch("copy_blocks", copy_blocks_kernel, dim3((unsigned)((a.total + 255) / 256)),
+                      dim3(256), stream, a);
+}
+
 }  // namespace pa

@@ -1,0 +1,189 @@
+"""The host block manager (pa_bm_*) on the CPU: allocation on demand, forks
+that share blocks, copy-on-write, release, tables -- and, end to end, that
+the tables it hands out make the paged oracle reproduce attention over each
+sequence's logical tokens.
+
+Which free block the manager picks is its own choice, so the tests check
+what is fixed (token order, sharing, refcounts, where copies are needed)
+and that everything else is valid (no block held twice unless shared, every
+block either free or held)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_decode_amd import binding as B
+
+
+def test_append_allocates_on_demand():
+    bm = B.BlockManager(10, 4)
+    bm.add(7)
+    s = bm.append(7, 6)
+    assert bm.num_free == 8  # ceil(6 / 4) blocks taken
+    blocks = s // 4
+    assert len(set(blocks[:4])) == 1 and len(set(blocks[4:])) == 1 and blocks[0] != blocks[4]
+    assert list(s % 4) == [0, 1, 2, 3, 0, 1]
+    s2 = bm.append(7, 3)  # fills the second block, then takes a third
+    assert list(s2 % 4) == [2, 3, 0] and s2[0] // 4 == blocks[4] and bm.num_free == 7
+    table, lens = bm.block_table([7], 5)
+    assert lens[0] == 9 and list(table[0, 3:]) == [-1, -1]
+    assert list(table[0, :3]) == [blocks[0], blocks[4], s2[2] // 4]
+    assert len(bm.append(7, 0)) == 0 and bm.num_free == 7
+
+
+def test_fork_shares_and_free_returns_blocks():
+    bm = B.BlockManager(6, 4)
+    bm.add(0)
+    bm.append(0, 8)  # two full blocks
+    bm.fork(0, 1)
+    t, lens = bm.block_table([0, 1], 4)
+    assert (t[0] == t[1]).all() and list(lens) == [8, 8]
+    assert all(bm.refcount(int(b)) == 2 for b in t[0, :2])
+    bm.append(1, 1)  # full last block: a new block, no copy
+    assert bm.take_copies()[0].size == 0
+    bm.free(0)
+    assert bm.num_free == 6 - 3 and all(bm.refcount(int(b)) == 1 for b in t[0, :2])
+    bm.free(1)
+    assert bm.num_free == 6
+
+
+def test_copy_on_write_of_a_shared_partial_block():
+    bm = B.BlockManager(8, 4)
+    bm.add(0)
+    bm.append(0, 6)  # block a full, block b holds 2 tokens
+    bm.fork(0, 1)
+    t0, _ = bm.block_table([0], 4)
+    a, b = int(t0[0, 0]), int(t0[0, 1])
+    s = bm.append(1, 1)  # child writes into shared b: copied first
+    src, dst = bm.take_copies()
+    assert list(src) == [b] and dst.size == 1 and int(dst[0]) not in (a, b)
+    assert s[0] == int(dst[0]) * 4 + 2
+    assert bm.refcount(b) == 1 and bm.refcount(int(dst[0])) == 1 and bm.refcount(a) == 2
+    s = bm.append(0, 1)  # the parent now owns b alone: writes in place
+    assert s[0] == b * 4 + 2 and bm.take_copies()[0].size == 0
+
+
+def test_out_of_blocks_leaves_state_unchanged():
+    bm = B.BlockManager(3, 4)
+    bm.add(0)
+    bm.append(0, 10)
+    before = bm.block_table([0], 4)
+    with pytest.raises(B.PAError) as e:
+        bm.append(0, 5)  # needs 2 more blocks, 0 free... 3 used
+    assert e.value.status == -6
+    after = bm.block_table([0], 4)
+    assert (before[0] == after[0]).all() and before[1][0] == after[1][0] == 10
+    bm.fork(0, 1)
+    with pytest.raises(B.PAError):
+        bm.append(1, 1)  # copy-on-write needs a block too
+    assert bm.take_copies()[0].size == 0
+
+
+def test_errors():
+    with pytest.raises(B.PAError):
+        B.BlockManager(0, 16)
+    bm = B.BlockManager(4, 16)
+    bm.add(1)
+    for f in (lambda: bm.add(1), lambda: bm.add(-2), lambda: bm.append(9, 1),
+              lambda: bm.fork(9, 3), lambda: bm.fork(1, 1), lambda: bm.free(9),
+              lambda: bm.append(1, -1), lambda: bm.block_table([9], 4)):
+        with pytest.raises(B.PAError):
+            f()
+    bm.append(1, 40)  # 3 blocks
+    with pytest.raises(B.PAError) as e:
+        bm.block_table([1], 2)
+    assert e.value.status == -3
+
+
+def run_scenario(seed, NB=48, Bs=4, Hkv=2, d=16, steps=120):
+    """Random adds / appends / forks / frees against a Python model of each
+    sequence's logical K/V rows; the pools are written through the slots
+    the manager returns (after applying its copy-on-write pairs)."""
+    rng = np.random.default_rng(seed)
+    bm = B.BlockManager(NB, Bs)
+    kp = np.full((NB, Bs, Hkv, d), np.nan, np.float32)
+    vp = np.full((NB, Bs, Hkv, d), np.nan, np.float32)
+    logical = {}  # seq -> (K rows list, V rows list)
+    next_id = 0
+    for _ in range(steps):
+        op = rng.integers(0, 4)
+        if op == 0 or not logical:
+            bm.add(next_id)
+            logical[next_id] = ([], [])
+            next_id += 1
+        elif op == 1:
+            sid = int(rng.choice(list(logical)))
+            n = int(rng.integers(1, 9))
+            try:
+                slots = bm.append(sid, n)
+            except B.PAError as e:
+                assert e.status == -6
+                continue
+            src, dst = bm.take_copies()
+            for a_, b_ in zip(src, dst):  # copy-on-write before writing
+                kp[b_] = kp[a_]
+                vp[b_] = vp[a_]
+            kn = rng.standard_normal((n, Hkv, d)).astype(np.float32)
+            vn = rng.standard_normal((n, Hkv, d)).astype(np.float32)
+            for i, x in enumerate(slots):
+                assert bm.refcount(int(x) // Bs) == 1  # written blocks are exclusive
+                kp[x // Bs, x % Bs] = kn[i]
+                vp[x // Bs, x % Bs] = vn[i]
+            logical[sid][0].extend(kn)
+            logical[sid][1].extend(vn)
+        elif op == 2:
+            sid = int(rng.choice(list(logical)))
+            bm.fork(sid, next_id)
+            logical[next_id] = (list(logical[sid][0]), list(logical[sid][1]))
+            next_id += 1
+        else:
+            sid = int(rng.choice(list(logical)))
+            bm.free(sid)
+            del logical[sid]
+    return bm, kp, vp, logical
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_random_scenario_tables_gather_the_logical_tokens(seed):
+    NB, Bs = 48, 4
+    bm, kp, vp, logical = run_scenario(seed, NB, Bs)
+    ids = sorted(logical)
+    MB = NB
+    table, lens = bm.block_table(ids, MB)
+    held = {}
+    for row, sid in zip(table, ids):
+        n = len(logical[sid][0])
+        nblk = -(-n // Bs)
+        assert (row[nblk:] == -1).all() and (row[:nblk] >= 0).all()
+        for b in row[:nblk]:
+            held[int(b)] = held.get(int(b), 0) + 1
+        if n:
+            t = np.arange(n)
+            got_k = kp[row[t // Bs], t % Bs]
+            got_v = vp[row[t // Bs], t % Bs]
+            assert np.array_equal(got_k, np.stack(logical[sid][0]))
+            assert np.array_equal(got_v, np.stack(logical[sid][1]))
+    # Every block is either free or held, with the refcount the tables imply.
+    assert bm.num_free + len(held) == NB
+    assert all(bm.refcount(b) == c for b, c in held.items())
+
+
+def test_random_scenario_attention_matches_dense():
+    """Decode through the manager's tables (paged oracle) equals attention
+    over each sequence's contiguous logical rows."""
+    Bs, Hkv, d, G = 4, 2, 16, 2
+    bm, kp, vp, logical = run_scenario(11, 48, Bs, Hkv, d)
+    ids = [s for s in sorted(logical) if logical[s][0]]
+    assert len(ids) >= 2
+    table, lens = bm.block_table(ids, 48)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((len(ids), Hkv * G, d)).astype(np.float32)
+    paged, _ = oracle.decode(q, kp, vp, table, lens, 0.25, "f32")
+    for i, sid in enumerate(ids):
+        K = np.stack(logical[sid][0]).astype(np.float64)  # [n, Hkv, d]
+        V = np.stack(logical[sid][1]).astype(np.float64)
+        for h in range(Hkv * G):
+            x = K[:, h // G] @ q[i, h].astype(np.float64) * 0.25
+            p = np.exp(x - x.max())
+            ref = (p / p.sum()) @ V[:, h // G]
+            assert np.allclose(paged[i, h], ref, rtol=0, atol=1e-12)
