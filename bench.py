@@ -153,13 +153,16 @@ def kernel_avg_ms(binding, name):
     return (ms / n if n else float("nan")), n
 
 
-def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype):
-    """Time pa_decode on a case, rotating over `copies` device copies of the
-    pools.  Returns a dict of timings."""
+def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
+                      prefix_len=None):
+    """Time pa_decode (or pa_decode_shared_prefix with ``prefix_len``) on a
+    case, rotating over `copies` device copies of the pools.  Returns a dict
+    of timings."""
     devs = [binding.upload_case(case) for _ in range(copies)]
     out = torch.empty(case.q.shape, dtype=out_dtype, device="cuda")
     calls = [binding.PreparedDecode(d["q"], d["k_pool"], d["v_pool"], d["block_table"],
-                                    d["context_lens"], case.scale, out) for d in devs]
+                                    d["context_lens"], case.scale, out, prefix_len)
+             for d in devs]
     plan = binding.decode_plan(devs[0]["q"], devs[0]["k_pool"], devs[0]["v_pool"],
                                devs[0]["block_table"], devs[0]["context_lens"], out)
     step = lambda i: calls[i % copies]()  # noqa: E731
@@ -173,12 +176,14 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype):
     timer.run(step, steps)
     binding.profiler_enable(False)
     part_ms, part_n = kernel_avg_ms(binding, "decode_partitions")
+    pre_ms, pre_n = kernel_avg_ms(binding, "prefill")
     binding.profiler_reset()
     del calls, devs
     torch.cuda.synchronize()
     binding.workspace_release()
     torch.cuda.empty_cache()
-    return dict(sec=sec, part_ms=part_ms, part_launches=part_n, plan=plan)
+    return dict(sec=sec, part_ms=part_ms, part_launches=part_n, plan=plan,
+                prefix_ms=pre_ms if pre_n else 0.0)
 
 
 def cpu_oracle_decode(case, budget_s=20.0):
@@ -300,12 +305,21 @@ def main():
                           logical - int(case.context_lens.sum()) * 8 * 128 * 2 * 2)
                 r = bench_decode_case(torch, binding, case, max(10, a.steps // 2), 3, 3,
                                       torch.bfloat16)
+                rc = bench_decode_case(torch, binding, case, max(10, a.steps // 2), 3, 3,
+                                       torch.bfloat16, prefix_len=case.meta["prefix_len"])
                 extra[f"prefix-shared-bf16-decode-B{B}"] = {
                     "unique_GB/s": round(unique / r["sec"] / 1e9, 1),
                     "frac_of_hbm_peak_unique": round(unique / r["sec"] / 1e9 / HBM_PEAK_GBS, 4),
                     "logical_GB/s": round(logical / r["sec"] / 1e9, 1),
                     "ms_per_step": round(r["sec"] * 1e3, 4),
                     "partition_kernel_avg_us": round(r["part_ms"] * 1e3, 2),
+                    "shared_prefix_call": {
+                        "unique_GB/s": round(unique / rc["sec"] / 1e9, 1),
+                        "frac_of_hbm_peak_unique": round(unique / rc["sec"] / 1e9 /
+                                                         HBM_PEAK_GBS, 4),
+                        "ms_per_step": round(rc["sec"] * 1e3, 4),
+                        "prefix_kernel_avg_us": round(rc["prefix_ms"] * 1e3, 2),
+                        "suffix_kernel_avg_us": round(rc["part_ms"] * 1e3, 2)},
                     "unique_bytes": unique, "logical_bytes": logical}
                 del case
         # ---------------- causal prefill, bf16 ---------------------------

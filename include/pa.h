@@ -178,6 +178,37 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
                 const pa_tensor* v_pool, void* stream);
 
 /*
+ * pa_decode_shared_prefix -- pa_decode for sequences whose first
+ * prefix_len tokens are one shared prefix stored in the same physical
+ * blocks ("FlashAttention and PagedAttention: two fixes for two different
+ * bottlenecks", "PagedAttention - How it works": sequences with a common
+ * prompt share its blocks).  The result is pa_decode's (same arguments and
+ * the same math, up to floating-point rounding); the work is split so that
+ * the prefix is read once per KV head instead of once per sequence:
+ *   1. every sequence's G query heads attend to the prefix keys together,
+ *      as one dense block on the matrix cores (the prefill kernel, keys
+ *      split into chunks), giving normalised partial outputs and
+ *      log-sum-exps;
+ *   2. the decode kernel attends each sequence's own keys
+ *      [prefix_len, n_s) and merges its parts with the prefix parts
+ *      (log-sum-exp merge), writing `out`.
+ *
+ *   prefix_len   host int, a multiple of the block size, 0 <= prefix_len
+ *                <= MB * B.  0 is plain pa_decode.
+ * Contract (device contents, not checked): n_s >= prefix_len for every s,
+ * and block_table[s][j] == block_table[0][j] for j < prefix_len / B.
+ * Supported: f16/bf16, d = 128 (other shapes return PA_ERR_UNSUPPORTED);
+ * the same G, B and strides as pa_decode.  The workspace (see pa_decode)
+ * also holds the prefix parts, n_chunks * S * H * (d + 1) * 4 bytes, where
+ * n_chunks <= ceil(prefix_len / 64) is chosen so that the prefix step has
+ * about one workgroup per compute unit.
+ */
+int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
+                            const pa_tensor* v_pool, const pa_tensor* block_table,
+                            const pa_tensor* context_lens, int32_t prefix_len, float scale,
+                            const pa_tensor* out, void* stream);
+
+/*
  * pa_copy_blocks -- copy whole physical blocks src[i] -> dst[i] in both
  * pools (the copy-on-write step of "FlashAttention and PagedAttention: two
  * fixes for two different bottlenecks", "PagedAttention - How it works":
@@ -285,7 +316,8 @@ int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor*
  * elapsed time is the kernel's own execution.
  * pa_profiler_read synchronises on the recorded events and adds their
  * elapsed times to per-kernel totals.  Kernel names: "decode_partitions",
- * "prefill", "write_kv", "copy_blocks".  Not meant for concurrent use from
+ * "prefill" (also the prefix step of pa_decode_shared_prefix), "write_kv",
+ * "copy_blocks".  Not meant for concurrent use from
  * several threads.
  */
 int pa_profiler_enable(int on);

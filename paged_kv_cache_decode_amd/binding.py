@@ -48,7 +48,7 @@ class PAError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ("pa_decode", "pa_prefill", "pa_write_kv", "pa_copy_blocks", "pa_status_string",
+EXPORTS = ("pa_decode", "pa_decode_shared_prefix", "pa_prefill", "pa_write_kv", "pa_copy_blocks", "pa_status_string",
            "pa_last_error", "pa_decode_plan", "pa_workspace_release", "pa_profiler_enable",
            "pa_profiler_reset", "pa_profiler_read", "pa_bm_create", "pa_bm_destroy",
            "pa_bm_num_free", "pa_bm_refcount", "pa_bm_add", "pa_bm_fork", "pa_bm_append",
@@ -66,6 +66,8 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(PaTensor)
     L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, ctypes.c_void_p]
+    L.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.c_float, P,
+                                          ctypes.c_void_p]
     L.pa_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                              P, ctypes.c_void_p]
     L.pa_write_kv.argtypes = [P, P, P, P, P, ctypes.c_void_p]
@@ -85,7 +87,8 @@ def lib():
     L.pa_bm_take_copies.argtypes = [V, I32P, I32P, ctypes.c_int32]
     L.pa_bm_free.argtypes = [V, ctypes.c_int64]
     L.pa_bm_block_table.argtypes = [V, I64P, ctypes.c_int32, ctypes.c_int32, I32P, I32P]
-    for f in ("pa_decode", "pa_prefill", "pa_write_kv", "pa_copy_blocks", "pa_decode_plan",
+    for f in ("pa_decode", "pa_decode_shared_prefix", "pa_prefill", "pa_write_kv",
+              "pa_copy_blocks", "pa_decode_plan",
               "pa_workspace_release", "pa_profiler_enable", "pa_profiler_read", "pa_bm_num_free",
               "pa_bm_refcount", "pa_bm_add", "pa_bm_fork", "pa_bm_append", "pa_bm_take_copies",
               "pa_bm_free", "pa_bm_block_table"):
@@ -146,6 +149,20 @@ def decode(q, k_pool, v_pool, block_table, context_lens, scale, out=None, out_dt
     o = describe(out)
     _check(L.pa_decode(*[ctypes.byref(a) for a in args], ctypes.c_float(scale),
                        ctypes.byref(o), _stream(stream)))
+    return out
+
+
+def decode_shared_prefix(q, k_pool, v_pool, block_table, context_lens, prefix_len, scale,
+                         out=None, out_dtype=None, stream=None):
+    """pa_decode for sequences sharing their first ``prefix_len`` tokens (in
+    the same physical blocks); see ``pa_decode_shared_prefix``."""
+    L = lib()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens)]
+    o = describe(out)
+    _check(L.pa_decode_shared_prefix(*[ctypes.byref(a) for a in args], int(prefix_len),
+                                     ctypes.c_float(scale), ctypes.byref(o), _stream(stream)))
     return out
 
 
@@ -279,19 +296,26 @@ def profiler_read(kernel: str):
 
 
 class PreparedDecode:
-    """A pa_decode call with its descriptors built once (for tight loops)."""
+    """A pa_decode call (or, with ``prefix_len``, a pa_decode_shared_prefix
+    call) with its descriptors built once (for tight loops)."""
 
-    def __init__(self, q, k_pool, v_pool, block_table, context_lens, scale, out):
+    def __init__(self, q, k_pool, v_pool, block_table, context_lens, scale, out,
+                 prefix_len=None):
         self._keep = (q, k_pool, v_pool, block_table, context_lens, out)
         self._args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens)]
         self._out = describe(out)
         self._refs = [ctypes.byref(x) for x in self._args]
         self._scale = ctypes.c_float(scale)
+        self._prefix = prefix_len
         self._L = lib()
 
     def __call__(self, stream=None):
-        _check(self._L.pa_decode(*self._refs, self._scale, ctypes.byref(self._out),
-                                 _stream(stream)))
+        if self._prefix is None:
+            _check(self._L.pa_decode(*self._refs, self._scale, ctypes.byref(self._out),
+                                     _stream(stream)))
+        else:
+            _check(self._L.pa_decode_shared_prefix(*self._refs, int(self._prefix), self._scale,
+                                                   ctypes.byref(self._out), _stream(stream)))
         return self._keep[-1]
 
 

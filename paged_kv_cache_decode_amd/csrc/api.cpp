@@ -237,6 +237,97 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_po
   return PA_OK;
 }
 
+int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
+                            const pa_tensor* v_pool, const pa_tensor* block_table,
+                            const pa_tensor* context_lens, int32_t prefix_len, float scale,
+                            const pa_tensor* out, void* stream_ptr) {
+  g_last_error.clear();
+  pa::DecodePlan plan;
+  int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out, 1, &plan,
+                           &g_last_error);
+  if (st) return st;
+  if (prefix_len < 0 || prefix_len % plan.B != 0 || (int64_t)prefix_len > (int64_t)plan.MB * plan.B)
+    return set_error(PA_ERR_ARG, "prefix_len %d must be a multiple of the block size %d in "
+                     "[0, %lld]", prefix_len, plan.B, (long long)plan.MB * plan.B);
+  if (prefix_len == 0 || plan.S == 0)
+    return pa_decode(q, k_pool, v_pool, block_table, context_lens, scale, out, stream_ptr);
+  if ((plan.dtype != PA_F16 && plan.dtype != PA_BF16) || plan.D != 128)
+    return set_error(PA_ERR_UNSUPPORTED, "the shared-prefix path needs f16/bf16 and d = 128");
+  st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out,
+                       decode_workers(q, k_pool), &plan, &g_last_error);
+  if (st) return st;
+
+  // Prefix part: the S query rows of every KV head against the prefix keys,
+  // one pseudo-sequence of S rows and prefix_len keys read through row 0 of
+  // the table, split into key chunks so that every CU gets a workgroup.
+  pa::PrefillPlan pp;
+  pp.dtype = plan.dtype;
+  pp.out_dtype = PA_F32;
+  pp.S = 1;
+  pp.T = plan.S;
+  pp.H = plan.H;
+  pp.Hkv = plan.Hkv;
+  pp.G = plan.G;
+  pp.D = plan.D;
+  pp.B = plan.B;
+  pp.MB = plan.MB;
+  pp.NB = plan.NB;
+  pp.max_query_len = plan.S;
+  pp.causal = 0;
+  pp.q_tiles = (plan.S + pa::kPrefillRows - 1) / pa::kPrefillRows;
+  pp.q = plan.q;
+  pp.q_st = plan.q_ss;
+  pp.q_sh = plan.q_sh;
+  pp.k = plan.k;
+  pp.v = plan.v;
+  pp.bt = plan.bt;  // row 0: the prefix blocks, common to all rows
+  pp.bt_ss = 0;
+  pp.scale = scale;
+  pp.fixed_L = plan.S;
+  pp.fixed_n = prefix_len;
+  const int ptiles = (prefix_len + 63) / 64;
+  const int base = pp.q_tiles * plan.Hkv;
+  int chunks = std::max(1, std::min(ptiles, (256 + base - 1) / base));
+  pp.chunk_tiles = (ptiles + chunks - 1) / chunks;
+  pp.n_chunks = (ptiles + pp.chunk_tiles - 1) / pp.chunk_tiles;
+  pp.part_rows = plan.S;
+  // Workspace: the decode counters plus one counter per (KV head, query
+  // tile) of the prefix step | decode partials | prefix chunk partials |
+  // merged prefix result.
+  const int64_t n_prefix_counters = (int64_t)plan.Hkv * pp.q_tiles;
+  const int64_t dec_counter_bytes = plan.counter_bytes;
+  plan.counter_bytes = ((int64_t)plan.S * plan.Hkv * 4 + n_prefix_counters * 4 + 255) / 256 * 256;
+  const int64_t dec_part = plan.ws_bytes - dec_counter_bytes;
+  const int64_t chunk_rows = (int64_t)pp.n_chunks * plan.S * plan.H;
+  const int64_t merged_rows = (int64_t)plan.S * plan.H;
+  const int64_t chunk_off = (dec_part + 255) / 256 * 256;
+  const int64_t merged_off = chunk_off + (chunk_rows * (plan.D + 1) * 4 + 255) / 256 * 256;
+  plan.ws_bytes = plan.counter_bytes + merged_off + merged_rows * (plan.D + 1) * 4;
+  if (log_enabled())
+    fprintf(stderr, "[pa] decode_shared_prefix S=%d prefix=%d chunks=%d x %d tiles workers=%d\n",
+            plan.S, prefix_len, pp.n_chunks, pp.chunk_tiles, plan.workers);
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  void* ws = nullptr;
+  st = acquire_workspace(&plan, stream, &ws);
+  if (st) return st;
+  uint8_t* parts = static_cast<uint8_t*>(ws) + plan.counter_bytes;
+  pp.counters = static_cast<int*>(ws) + (int64_t)plan.S * plan.Hkv;
+  pp.part_o = reinterpret_cast<float*>(parts + chunk_off);
+  pp.part_lse = pp.part_o + chunk_rows * plan.D;
+  pp.merged_o = reinterpret_cast<float*>(parts + merged_off);
+  pp.merged_lse = pp.merged_o + merged_rows * plan.D;
+  hipError_t e = pa::launch_prefill(pp, stream);
+  if (e != hipSuccess)
+    return set_error(PA_ERR_LAUNCH, "shared-prefix launch: %s", hipGetErrorString(e));
+  plan.key_begin = prefix_len;
+  plan.pre_o = pp.merged_o;
+  plan.pre_lse = pp.merged_lse;
+  e = pa::launch_decode(plan, ws, stream);
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 int pa_workspace_release(void* stream_ptr) {
   g_last_error.clear();
   int dev = -1;

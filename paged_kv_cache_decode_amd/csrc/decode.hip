@@ -89,6 +89,15 @@ struct DecodeArgs {
                     // between calls
   int S, H, Hkv, W, bs_shift;
   float scale_log2;  // scale * log2(e)
+  // Shared prefix (cascade): keys [0, key_begin) of every sequence were
+  // attended by an earlier kernel, whose result per (s, h) is the normalised
+  // pre_o [S, H, D] with log2-sum-exp pre_lse [S, H].  This kernel attends
+  // keys [key_begin, n_s): the first piece of each unit starts its online
+  // softmax from the prefix result instead of from zero.  key_begin = 0 and
+  // pre_o = nullptr for plain decode.
+  int key_begin;
+  const float* pre_o;
+  const float* pre_lse;
 };
 
 // S = Q K^T on matrix cores for one 16-key tile.  Returns, per lane, the
@@ -185,6 +194,7 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, in
 #pragma unroll
   for (int e = 0; e < kV; ++e) acc[e] = 0.f;
   auto add = [&](float lse, const float* o) {
+    if (lse == -INFINITY) return;  // a part with no keys
     const float mn = fmaxf(M, lse);
     const float sa = fast_exp2(M - mn), sb = fast_exp2(lse - mn);
     wsum = fmaf(wsum, sa, sb);
@@ -212,23 +222,32 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, in
     load_partial<kV>(a.part_o + slot * G * D + idx0, o);
     add(lse, o);
   }
-  const float inv = 1.f / wsum;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int64_t ob = (int64_t)s * a.o_ss + (int64_t)(g * G + h) * a.o_sh + d0;
 #pragma unroll
   for (int e = 0; e < kV; ++e) store_out<T>(a.out, ob + e, acc[e] * inv, a.out_f32 != 0);
 }
 
-// Units with an empty context are in no worker's slice; their output is
-// zero.  Worker i writes units i, i + W, ... (after its own slice, so that
-// the check is off the path to the first K/V loads).
+// Units with no key to attend here are in no worker's slice: their output
+// is zero, or, with a shared prefix, the prefix's merged parts.  Worker i
+// writes units i, i + W, ... (after its own slice, so that the check is off
+// the path to the first K/V loads).
 template <class T, int D, int G>
 __device__ __forceinline__ void zero_empty_units(const DecodeArgs& a, int worker, int lane) {
   for (int u = worker; u < a.S * a.Hkv; u += a.W) {
     const int su = u % a.S, gu = u / a.S;
-    if (as_const(a.cl)[su] == 0) {
-      for (int i = lane; i < G * D; i += 64)
-        store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
-                     0.f, a.out_f32 != 0);
+    if (as_const(a.cl)[su] <= a.key_begin) {
+      if (a.pre_o) {
+        // Only the shared prefix: its result is the whole result.
+        const int64_t row = (int64_t)su * a.H + gu * G;
+        for (int i = lane; i < G * D; i += 64)
+          store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
+                       a.pre_o[row * D + i], a.out_f32 != 0);
+      } else {
+        for (int i = lane; i < G * D; i += 64)
+          store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
+                       0.f, a.out_f32 != 0);
+      }
     }
   }
 }
@@ -255,12 +274,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   // ---- this worker's slice of the global tile list ----
   // Tiles per KV head over all sequences (the list is g-major).  With at
   // most 64 sequences one load of the lengths serves both passes.
-  const int lane_len = lane < a.S ? as_const(a.cl)[lane] : 0;
+  // Keys this kernel attends per sequence: n_s - key_begin.
+  const int lane_len = lane < a.S ? max(as_const(a.cl)[lane] - a.key_begin, 0) : 0;
   const int lane_tiles = tiles_of(lane_len);
   int64_t t_all = wave_sum_i64(lane_tiles);
   for (int c0 = 64; c0 < a.S; c0 += 64) {
     const int s = c0 + lane;
-    t_all += wave_sum_i64(s < a.S ? (int64_t)tiles_of(as_const(a.cl)[s]) : 0);
+    t_all += wave_sum_i64(
+        s < a.S ? (int64_t)tiles_of(max(as_const(a.cl)[s] - a.key_begin, 0)) : 0);
   }
   const int64_t total = t_all * a.Hkv;
   const int64_t per = (total + a.W - 1) / a.W;
@@ -282,7 +303,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     for (int c0 = 0; c0 < a.S; c0 += 64) {
       const int ss = c0 + lane;
       const int64_t tl =
-          c0 == 0 ? lane_tiles : (ss < a.S ? (int64_t)tiles_of(as_const(a.cl)[ss]) : 0);
+          c0 == 0 ? lane_tiles
+                  : (ss < a.S ? (int64_t)tiles_of(max(as_const(a.cl)[ss] - a.key_begin, 0)) : 0);
       const int64_t incl = wave_incl_scan_i64(tl, lane);
       const int64_t chunk = uniform_i64(__shfl(incl, 63));
       if (pre + chunk > r) {
@@ -316,7 +338,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     s = uniform_i(s);
     g = uniform_i(g);
     // With at most 64 sequences every length is already in a register.
-    const int n = a.S <= 64 ? __builtin_amdgcn_readlane(lane_len, s) : as_const(a.cl)[s];
+    const int n = a.S <= 64 ? __builtin_amdgcn_readlane(lane_len, s)
+                            : max(as_const(a.cl)[s] - a.key_begin, 0);
     const int ts = tiles_of(n);
     if (t >= unit_first + ts) {  // empty or finished unit: next sequence / head
       unit_first += ts;
@@ -358,11 +381,27 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 #pragma unroll
       for (int e = 0; e < kE; ++e) acc[h][e] = 0.f;
     }
+    if (a.pre_o && j0 == 0) {
+      // The unit's first piece continues the shared prefix's softmax: its
+      // state (max lse, sum 1, output o) enters once -- the sum in one lane
+      // of each 16-lane row (rows are summed at the end), the output in the
+      // lanes of V row 0 (lanes sharing a column are summed at the end).
+      const int64_t row = (int64_t)s * a.H + hq0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        m[h] = a.pre_lse[row + h];
+        l_lane[h] = r16 == 0 ? 1.f : 0.f;
+        if (lane < Geo::kLPR) {
+#pragma unroll
+          for (int e = 0; e < kE; ++e) acc[h][e] = a.pre_o[(row + h) * D + lane * kE + e];
+        }
+      }
+    }
 
     u32x4_t kr[kDepth][Geo::kKLoads], vr[kDepth][Geo::kVLoads];
 
     auto load_tile = [&](int k, u32x4_t* kd, u32x4_t* vd) {
-      const int key0 = uniform_i((j0 + min(k, ntile - 1)) * kTileKeys);
+      const int key0 = uniform_i(a.key_begin + (j0 + min(k, ntile - 1)) * kTileKeys);
       const int phys = bt_row[key0 >> a.bs_shift];
       const int64_t row0 = (int64_t)phys * blk_stride + (int64_t)(key0 & bmask) * tok_stride;
       const uint8_t* kb = kbase + row0;
@@ -628,6 +667,9 @@ hipError_t launch_decode(const DecodePlan& pl, void* workspace, hipStream_t stre
   a.W = pl.workers;
   a.bs_shift = __builtin_ctz(pl.B);
   a.scale_log2 = pl.scale * 1.4426950408889634f;
+  a.key_begin = pl.key_begin;
+  a.pre_o = pl.pre_o;
+  a.pre_lse = pl.pre_lse;
   switch (pl.dtype) {
     case PA_F32: return dispatch_shape<TF32>(pl, a, stream);
     case PA_F16: return dispatch_shape<TF16>(pl, a, stream);

@@ -43,6 +43,11 @@ struct DecodePlan {
   void* out = nullptr;
   int64_t o_ss = 0, o_sh = 0;
   float scale = 0.f;
+  // Shared prefix: keys [0, key_begin) were attended by the prefix step,
+  // whose merged result per (s, h) is pre_o [S, H, D] / pre_lse [S, H].
+  int key_begin = 0;
+  const float* pre_o = nullptr;
+  const float* pre_lse = nullptr;
 };
 
 struct PrefillPlan {
@@ -65,6 +70,16 @@ struct PrefillPlan {
   void* out = nullptr;
   int64_t o_st = 0, o_sh = 0;
   float scale = 0.f;
+  // Shared-prefix attention (decode with a common prefix): one sequence given
+  // by value and key chunks writing partial results; see prefill.hip.
+  int fixed_L = -1, fixed_n = 0;
+  int n_chunks = 1, chunk_tiles = 1 << 30;
+  int64_t part_rows = 0;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  int* counters = nullptr;
+  float* merged_o = nullptr;
+  float* merged_lse = nullptr;
 };
 
 // Query positions per prefill workgroup (all G heads of one KV head).

@@ -71,10 +71,34 @@ struct PrefillArgs {
   int out_f32;
   int S, Hkv, MB, q_tiles, bs_shift, causal;
   uint32_t q_sign;     // XORed into Q's 16-bit lanes (0x80008000 when scale < 0)
-  int64_t n_wg;        // real workgroups (q_tiles * Hkv * S)
+  int64_t n_wg;        // real workgroups (q_tiles * Hkv * S * n_chunks)
   int64_t wg_per_xcd;  // ceil(n_wg / 8)
   float c;             // |scale| * log2(e)
+  // One sequence given by value (fixed_L >= 0): L = fixed_L rows, n =
+  // fixed_n keys; qsl / cl are not read.
+  int fixed_L, fixed_n;
+  // Keys split into n_chunks chunks of chunk_tiles 64-key tiles; with
+  // part_o set, each workgroup writes its normalised partial output and
+  // log2-sum-exp instead of `out`:
+  //   part_o [n_chunks, H, d, part_rows] f32, part_lse [n_chunks, H, part_rows].
+  int n_chunks, chunk_tiles, H;
+  int64_t part_rows;
+  float* part_o;
+  float* part_lse;
+  // With part_o set: the last of a (KV head, query tile)'s n_chunks
+  // workgroups to finish (counted in counters [Hkv * q_tiles], zero between
+  // calls) merges the chunks into merged_o [part_rows, H, d] and
+  // merged_lse [part_rows, H].
+  int* counters;
+  float* merged_o;
+  float* merged_lse;
 };
+
+// Chunk partials cross workgroups (and XCDs, whose L2 caches are not
+// coherent with each other): they are written with relaxed device-scope
+// atomic stores, which the hardware writes through to the coherent level
+// (the sc1 bit) without flushing the L2; the merging workgroup invalidates
+// its L2 once (agent-scope acquire) and then reads them with plain loads.
 
 template <class T>
 __device__ __forceinline__ f32x16_t mfma_qk(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -137,8 +161,10 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   // XCD-aware order: hardware workgroup b runs on XCD b % 8; give each XCD
   // a contiguous slice of the logical order (g, s, query tile descending).
   const int64_t bid = blockIdx.x;
-  const int64_t logical = (bid & 7) * a.wg_per_xcd + (bid >> 3);
-  if (logical >= a.n_wg) return;
+  const int64_t logical_c = (bid & 7) * a.wg_per_xcd + (bid >> 3);
+  if (logical_c >= a.n_wg) return;
+  const int chunk = (int)(logical_c % a.n_chunks);
+  const int64_t logical = logical_c / a.n_chunks;
   const int per_g = a.S * a.q_tiles;
   const int g = (int)(logical / per_g);
   const int rem = (int)(logical % per_g);
@@ -146,9 +172,9 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   const int qt = a.q_tiles - 1 - rem % a.q_tiles;
 
   const const_i32_ptr qsl = as_const(a.qsl);
-  const int q0 = qsl[s];
-  const int L = qsl[s + 1] - q0;
-  const int n = as_const(a.cl)[s];
+  const int q0 = a.fixed_L >= 0 ? 0 : qsl[s];
+  const int L = a.fixed_L >= 0 ? a.fixed_L : qsl[s + 1] - q0;
+  const int n = a.fixed_L >= 0 ? a.fixed_n : as_const(a.cl)[s];
   if (qt * kPrefillRows >= L) return;
 
   const int tid = threadIdx.x;
@@ -390,16 +416,19 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
     pv_half(vl, 1, pf1);
   };
 
-  if (ntk > 0) {
-    load_tile(0);
-    store_tile(0, 0);
-    if (ntk > 1) load_tile(1);
+  // This workgroup's tiles: [kt0, kt1) (all of [0, ntk) without chunking).
+  const int kt0 = min(ntk, chunk * a.chunk_tiles);
+  const int kt1 = min(ntk, kt0 + a.chunk_tiles);
+  if (kt0 < kt1) {
+    load_tile(kt0);
+    store_tile(kt0, kt0 & 1);
+    if (kt0 + 1 < kt1) load_tile(kt0 + 1);
   }
-  for (int kt = 0; kt < ntk; ++kt) {
+  for (int kt = kt0; kt < kt1; ++kt) {
     __syncthreads();  // tile kt is in buffer kt & 1; buffer (kt+1) & 1 is free
-    if (kt + 1 < ntk) {
+    if (kt + 1 < kt1) {
       store_tile(kt + 1, (kt + 1) & 1);
-      if (kt + 2 < ntk) load_tile(kt + 2);
+      if (kt + 2 < kt1) load_tile(kt + 2);
     }
     if (kt < full) {
       compute_tile(kt, kt & 1, std::false_type{});
@@ -408,9 +437,104 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
     }
   }
 
-  if (!row_ok) return;
   const float l_tot = l_lane + swap_halves(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (a.part_o) {
+    // Partial result of this key chunk: o / l and m + log2 l (log2 units of
+    // the scaled scores; -inf when the chunk held no visible key).  Lane
+    // (r32, hi) holds columns md*32 + 8*rg + 4*hi + 0..3 of its row.
+    const float lse = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+    const int64_t row = q0 + my_i;
+    // Chunk partials are stored row-fastest, [chunk][H][d][rows]: the 32
+    // lanes of a store instruction (32 consecutive rows) write 128
+    // contiguous bytes, which the write-through stores need to stay whole.
+    const int64_t cbase = ((int64_t)chunk * a.H + hq) * kD;
+    if (row_ok) {
+#pragma unroll
+      for (int md = 0; md < kD / 32; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = md * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          __hip_atomic_store(a.part_o + (cbase + d) * a.part_rows + row, acc_o[md][r] * inv,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      if (hi == 0)
+        __hip_atomic_store(a.part_lse + ((int64_t)chunk * a.H + hq) * a.part_rows + row, lse,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Count this chunk once every wave's stores have completed; the last
+    // chunk's workgroup merges all chunks of its rows.
+    __shared__ int last_chunk;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    int* counter = a.counters + (int64_t)g * a.q_tiles + qt;
+    if (tid == 0) {
+      const int done =
+          __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_chunk = done == a.n_chunks - 1;
+    }
+    __syncthreads();
+    if (!last_chunk) return;
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The other chunks' stores reached the coherent level before they were
+    // counted; drop this XCD's stale L2 lines once, then read them with
+    // ordinary (cached, wide) loads.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!row_ok) return;
+    // Log-sum-exp merge over the chunks (this chunk's part is still in
+    // registers): first the maximum and the weight sum, then the weighted
+    // outputs one 32-column group at a time (few registers live).
+    auto chunk_lse = [&](int c) {
+      return a.part_lse[((int64_t)c * a.H + hq) * a.part_rows + row];
+    };
+    float M = lse;
+    for (int c = 0; c < a.n_chunks; ++c)
+      if (c != chunk) M = fmaxf(M, chunk_lse(c));
+    auto weight = [&](float l) { return l == -INFINITY ? 0.f : fast_exp2(l - M); };
+    float wsum = weight(lse);
+    for (int c = 0; c < a.n_chunks; ++c)
+      if (c != chunk) wsum += weight(chunk_lse(c));
+    const float w_own = weight(lse) * inv;
+    const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int64_t mrow = row * a.H + hq;
+    float* mo = a.merged_o + mrow * kD;
+#pragma unroll
+    for (int md = 0; md < kD / 32; ++md) {
+      float o[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] = acc_o[md][r] * w_own;
+      // Four chunks' loads in flight at a time; slots past the end or equal
+      // to this chunk read this chunk's (valid) part with weight zero.
+      for (int c0 = 0; c0 < a.n_chunks; c0 += 4) {
+        float w[4], v[4][16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u;
+          const bool use = c < a.n_chunks && c != chunk;
+          w[u] = use ? weight(chunk_lse(c)) : 0.f;
+          const float* po =
+              a.part_o + ((int64_t)(use ? c : chunk) * a.H + hq) * kD * a.part_rows + row;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            v[u][r] = po[(int64_t)(md * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)) * a.part_rows];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[r] = fmaf(w[u], v[u][r], o[r]);
+      }
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *reinterpret_cast<f32x4_t*>(mo + md * 32 + 8 * rg + 4 * hi) =
+            f32x4_t{o[4 * rg] * winv, o[4 * rg + 1] * winv, o[4 * rg + 2] * winv,
+                    o[4 * rg + 3] * winv};
+    }
+    if (hi == 0) a.merged_lse[mrow] = wsum > 0.f ? M + __log2f(wsum) : -INFINITY;
+    return;
+  }
+  if (!row_ok) return;
   const int64_t obase = (int64_t)(q0 + my_i) * a.o_st + (int64_t)hq * a.o_sh;
 #pragma unroll
   for (int md = 0; md < kD / 32; ++md)
@@ -481,7 +605,18 @@ hipError_t launch_prefill(const PrefillPlan& pl, hipStream_t stream) {
   // that the softmax always works with c >= 0.
   a.q_sign = pl.scale < 0.f ? 0x80008000u : 0u;
   a.c = (pl.scale < 0.f ? -pl.scale : pl.scale) * 1.4426950408889634f;
-  a.n_wg = (int64_t)pl.q_tiles * pl.Hkv * pl.S;
+  a.fixed_L = pl.fixed_L;
+  a.fixed_n = pl.fixed_n;
+  a.n_chunks = pl.n_chunks;
+  a.chunk_tiles = pl.chunk_tiles;
+  a.H = pl.H;
+  a.part_rows = pl.part_rows;
+  a.part_o = pl.part_o;
+  a.part_lse = pl.part_lse;
+  a.counters = pl.counters;
+  a.merged_o = pl.merged_o;
+  a.merged_lse = pl.merged_lse;
+  a.n_wg = (int64_t)pl.q_tiles * pl.Hkv * pl.S * pl.n_chunks;
   a.wg_per_xcd = (a.n_wg + 7) / 8;
   if (a.n_wg == 0) return hipSuccess;
   switch (pl.dtype) {
