@@ -44,6 +44,14 @@
  *     [0, NB) for j < ceil(n_s / B).  Entries at j >= ceil(n_s / B) and pool
  *     slots at or past n_s are never used (they may hold anything, NaN
  *     included).
+ *   - Graph capture: pa_decode, pa_decode_shared_prefix, pa_prefill,
+ *     pa_write_kv and pa_copy_blocks issue only kernel launches once a
+ *     decode call's workspace exists, so they can be captured into a HIP
+ *     graph and replayed (a replay reads the buffers' contents at replay
+ *     time).  A decode call that would have to grow its stream's workspace
+ *     during a capture returns PA_ERR_ALLOC instead: make one call of the
+ *     same (or larger) size on that stream before capturing.  Dispatches
+ *     recorded into a graph are not timed by the profiler.
  */
 #ifndef PA_H_
 #define PA_H_

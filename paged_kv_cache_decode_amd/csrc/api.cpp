@@ -81,8 +81,19 @@ void set_last_error(const char* msg) { g_last_error = msg; }
 
 bool profiler_enabled() { return g_prof_on; }
 
-KernelTimer::KernelTimer(const char* name) : name_(name) {
+// True when `stream` is being captured into a graph.  (A stream whose state
+// cannot be read -- no device -- counts as not captured; the calls that
+// follow report the real failure.)
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
+KernelTimer::KernelTimer(const char* name, hipStream_t stream) : name_(name) {
   if (!g_prof_on) return;
+  // A dispatch recorded into a graph is not timed: its events would be
+  // recorded once, at capture, not at each replay.
+  if (capturing(stream)) return;
   if (hipEventCreate(&start_) != hipSuccess) start_ = nullptr;
   if (start_ && hipEventCreate(&stop_) != hipSuccess) {
     (void)hipEventDestroy(start_);
@@ -161,6 +172,13 @@ int acquire_workspace(pa::DecodePlan* plan, hipStream_t stream, void** out) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   StreamWorkspace& w = g_ws[{dev, static_cast<void*>(stream)}];
   if (w.ptr == nullptr || w.counter_bytes < need_c || w.part_bytes < need_p) {
+    // Growing records an allocation and a memset; inside a graph capture
+    // neither is wanted (a memset node's effect would not repeat at each
+    // replay the way the kernels expect).  The buffer must be sized first.
+    if (pa::capturing(stream))
+      return set_error(PA_ERR_ALLOC, "the workspace of this stream must grow to %lld bytes, "
+                       "which is not done during graph capture: make one call of this size "
+                       "on the stream before capturing", (long long)plan->ws_bytes);
     if (forced_alloc_failure())
       return set_error(PA_ERR_ALLOC, "workspace of %lld bytes: allocation failure forced by "
                        "PA_TEST_FAIL_ALLOC", (long long)plan->ws_bytes);

@@ -28,7 +28,7 @@ hipError_t launch_copy_blocks(const CopyBlocksPlan& plan, hipStream_t stream);
 // pair is queued for reading by commit() and released otherwise.
 bool profiler_enabled();
 struct KernelTimer {
-  explicit KernelTimer(const char* name);
+  KernelTimer(const char* name, hipStream_t stream);
   ~KernelTimer();
   KernelTimer(const KernelTimer&) = delete;
   KernelTimer& operator=(const KernelTimer&) = delete;

@@ -14,7 +14,7 @@ namespace pa {
 template <class... Params, class... Args>
 hipError_t timed_launch(const char* name, void (*kernel)(Params...), dim3 grid, dim3 block,
                         hipStream_t stream, Args... args) {
-  KernelTimer t(name);
+  KernelTimer t(name, stream);
   if (t.start_)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t.start_, t.stop_, 0, args...);
   else

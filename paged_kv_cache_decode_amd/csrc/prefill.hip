@@ -483,20 +483,19 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
     // ordinary (cached, wide) loads.
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (!row_ok) return;
-    // Log-sum-exp merge over the chunks (this chunk's part is still in
-    // registers): first the maximum and the weight sum, then the weighted
-    // outputs one 32-column group at a time (few registers live).
+    // Log-sum-exp merge over the chunks, all read back from memory in chunk
+    // order (this chunk's own part too), so that the result does not depend
+    // on which chunk finished last: first the maximum and the weight sum,
+    // then the weighted outputs one 32-column group at a time (few registers
+    // live).
     auto chunk_lse = [&](int c) {
       return a.part_lse[((int64_t)c * a.H + hq) * a.part_rows + row];
     };
-    float M = lse;
-    for (int c = 0; c < a.n_chunks; ++c)
-      if (c != chunk) M = fmaxf(M, chunk_lse(c));
+    float M = -INFINITY;
+    for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, chunk_lse(c));
     auto weight = [&](float l) { return l == -INFINITY ? 0.f : fast_exp2(l - M); };
-    float wsum = weight(lse);
-    for (int c = 0; c < a.n_chunks; ++c)
-      if (c != chunk) wsum += weight(chunk_lse(c));
-    const float w_own = weight(lse) * inv;
+    float wsum = 0.f;
+    for (int c = 0; c < a.n_chunks; ++c) wsum += weight(chunk_lse(c));
     const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
     const int64_t mrow = row * a.H + hq;
     float* mo = a.merged_o + mrow * kD;
@@ -504,18 +503,18 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
     for (int md = 0; md < kD / 32; ++md) {
       float o[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] = acc_o[md][r] * w_own;
-      // Four chunks' loads in flight at a time; slots past the end or equal
-      // to this chunk read this chunk's (valid) part with weight zero.
+      for (int r = 0; r < 16; ++r) o[r] = 0.f;
+      // Four chunks' loads in flight at a time; slots past the end read
+      // chunk 0's (valid) part with weight zero.
       for (int c0 = 0; c0 < a.n_chunks; c0 += 4) {
         float w[4], v[4][16];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int c = c0 + u;
-          const bool use = c < a.n_chunks && c != chunk;
+          const bool use = c < a.n_chunks;
           w[u] = use ? weight(chunk_lse(c)) : 0.f;
           const float* po =
-              a.part_o + ((int64_t)(use ? c : chunk) * a.H + hq) * kD * a.part_rows + row;
+              a.part_o + ((int64_t)(use ? c : 0) * a.H + hq) * kD * a.part_rows + row;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             v[u][r] = po[(int64_t)(md * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)) * a.part_rows];
