@@ -195,11 +195,12 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
  * the prefix is read once per KV head instead of once per sequence:
  *   1. every sequence's G query heads attend to the prefix keys together,
  *      as one dense block on the matrix cores (the prefill kernel, keys
- *      split into chunks), giving normalised partial outputs and
+ *      split into at most 4 chunks), giving normalised partial outputs and
  *      log-sum-exps;
  *   2. the decode kernel attends each sequence's own keys
- *      [prefix_len, n_s) and merges its parts with the prefix parts
- *      (log-sum-exp merge), writing `out`.
+ *      [prefix_len, n_s), starting each (sequence, KV head) from the
+ *      log-sum-exp merge of its prefix chunks, and merges its own parts as
+ *      pa_decode does, writing `out`.
  *
  *   prefix_len   host int, a multiple of the block size, 0 <= prefix_len
  *                <= MB * B.  0 is plain pa_decode.
@@ -208,8 +209,7 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
  * Supported: f16/bf16, d = 128 (other shapes return PA_ERR_UNSUPPORTED);
  * the same G, B and strides as pa_decode.  The workspace (see pa_decode)
  * also holds the prefix parts, n_chunks * S * H * (d + 1) * 4 bytes, where
- * n_chunks <= ceil(prefix_len / 64) is chosen so that the prefix step has
- * about one workgroup per compute unit.
+ * n_chunks <= min(4, ceil(prefix_len / 64)).
  */
 int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
                             const pa_tensor* v_pool, const pa_tensor* block_table,

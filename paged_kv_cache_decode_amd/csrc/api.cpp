@@ -305,22 +305,16 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   pp.fixed_n = prefix_len;
   const int ptiles = (prefix_len + 63) / 64;
   const int base = pp.q_tiles * plan.Hkv;
-  int chunks = std::max(1, std::min(ptiles, (256 + base - 1) / base));
+  int chunks = std::max(1, std::min({ptiles, (256 + base - 1) / base, pa::kMaxPrefixChunks}));
   pp.chunk_tiles = (ptiles + chunks - 1) / chunks;
   pp.n_chunks = (ptiles + pp.chunk_tiles - 1) / pp.chunk_tiles;
   pp.part_rows = plan.S;
-  // Workspace: the decode counters plus one counter per (KV head, query
-  // tile) of the prefix step | decode partials | prefix chunk partials |
-  // merged prefix result.
-  const int64_t n_prefix_counters = (int64_t)plan.Hkv * pp.q_tiles;
-  const int64_t dec_counter_bytes = plan.counter_bytes;
-  plan.counter_bytes = ((int64_t)plan.S * plan.Hkv * 4 + n_prefix_counters * 4 + 255) / 256 * 256;
-  const int64_t dec_part = plan.ws_bytes - dec_counter_bytes;
+  // Workspace: the decode counters | decode partials | prefix chunk
+  // partials (merged by the decode kernel as it starts each unit).
+  const int64_t dec_part = plan.ws_bytes - plan.counter_bytes;
   const int64_t chunk_rows = (int64_t)pp.n_chunks * plan.S * plan.H;
-  const int64_t merged_rows = (int64_t)plan.S * plan.H;
   const int64_t chunk_off = (dec_part + 255) / 256 * 256;
-  const int64_t merged_off = chunk_off + (chunk_rows * (plan.D + 1) * 4 + 255) / 256 * 256;
-  plan.ws_bytes = plan.counter_bytes + merged_off + merged_rows * (plan.D + 1) * 4;
+  plan.ws_bytes = plan.counter_bytes + chunk_off + chunk_rows * (plan.D + 1) * 4;
   if (log_enabled())
     fprintf(stderr, "[pa] decode_shared_prefix S=%d prefix=%d chunks=%d x %d tiles workers=%d\n",
             plan.S, prefix_len, pp.n_chunks, pp.chunk_tiles, plan.workers);
@@ -330,17 +324,15 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   st = acquire_workspace(&plan, stream, &ws);
   if (st) return st;
   uint8_t* parts = static_cast<uint8_t*>(ws) + plan.counter_bytes;
-  pp.counters = static_cast<int*>(ws) + (int64_t)plan.S * plan.Hkv;
   pp.part_o = reinterpret_cast<float*>(parts + chunk_off);
   pp.part_lse = pp.part_o + chunk_rows * plan.D;
-  pp.merged_o = reinterpret_cast<float*>(parts + merged_off);
-  pp.merged_lse = pp.merged_o + merged_rows * plan.D;
   hipError_t e = pa::launch_prefill(pp, stream);
   if (e != hipSuccess)
     return set_error(PA_ERR_LAUNCH, "shared-prefix launch: %s", hipGetErrorString(e));
   plan.key_begin = prefix_len;
-  plan.pre_o = pp.merged_o;
-  plan.pre_lse = pp.merged_lse;
+  plan.n_pre = pp.n_chunks;
+  plan.pre_o = pp.part_o;
+  plan.pre_lse = pp.part_lse;
   e = pa::launch_decode(plan, ws, stream);
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
   return PA_OK;

@@ -90,12 +90,14 @@ struct DecodeArgs {
   int S, H, Hkv, W, bs_shift;
   float scale_log2;  // scale * log2(e)
   // Shared prefix (cascade): keys [0, key_begin) of every sequence were
-  // attended by an earlier kernel, whose result per (s, h) is the normalised
-  // pre_o [S, H, D] with log2-sum-exp pre_lse [S, H].  This kernel attends
-  // keys [key_begin, n_s): the first piece of each unit starts its online
-  // softmax from the prefix result instead of from zero.  key_begin = 0 and
+  // attended by an earlier kernel in n_pre key chunks, whose normalised
+  // partial results are pre_o [n_pre, H, S, D] with log2-sum-exp pre_lse
+  // [n_pre, H, S].  This kernel attends keys [key_begin, n_s): the first
+  // piece of each unit merges the chunks (log-sum-exp) and starts its online
+  // softmax from that state instead of from zero.  key_begin = 0 and
   // pre_o = nullptr for plain decode.
   int key_begin;
+  int n_pre;
   const float* pre_o;
   const float* pre_lse;
 };
@@ -178,6 +180,56 @@ __device__ __forceinline__ void load_partial(const float* p, float* o) {
   }
 }
 
+// The shared prefix's merged state for unit (s, g), from its n_pre key
+// chunks, computed by the whole wave: lane l owns kV = G*D/64 consecutive
+// values of the unit's [G][D] output.
+//   M = max_c lse_c,  W = sum_c 2^(lse_c - M)  (the prefix's softmax sum
+//   relative to M),  o = sum_c 2^(lse_c - M) o_c  (unnormalised, relative
+//   to M),
+// for the lane's head (M, W) and values (o).  Loading (all chunks' loads in
+// flight together) and merging are separate steps, so that other loads can
+// be issued in between.
+template <int D, int G>
+struct PrefixParts {
+  static constexpr int kV = G * D / 64;
+  float lse[kMaxPrefixChunks];
+  float ov[kMaxPrefixChunks][kV];
+
+  __device__ __forceinline__ void load(const DecodeArgs& a, int s, int g, int lane) {
+    const int idx0 = lane * kV;
+    const int hq = g * G + idx0 / D, d0 = idx0 % D;
+#pragma unroll
+    for (int c = 0; c < kMaxPrefixChunks; ++c) {
+      if (c < a.n_pre) {
+        const int64_t row = ((int64_t)c * a.H + hq) * a.S + s;
+        lse[c] = a.pre_lse[row];
+#pragma unroll
+        for (int e = 0; e < kV; ++e) ov[c][e] = a.pre_o[row * D + d0 + e];
+      } else {
+        lse[c] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kV; ++e) ov[c][e] = 0.f;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void merge(float& M, float& W, float* o) const {
+    M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMaxPrefixChunks; ++c) M = fmaxf(M, lse[c]);
+    W = 0.f;
+#pragma unroll
+    for (int e = 0; e < kV; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxPrefixChunks; ++c) {
+      const float w = lse[c] == -INFINITY ? 0.f : fast_exp2(lse[c] - M);
+      W += w;
+#pragma unroll
+      for (int e = 0; e < kV; ++e) o[e] = fmaf(w, ov[c][e], o[e]);
+    }
+  }
+};
+
 // Log-sum-exp merge of the np partitions of unit (g, s), held in slots
 // slot0 .. slot0+np-1, by one wave:
 //   out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),  M = max_p lse_p,
@@ -238,11 +290,19 @@ __device__ __forceinline__ void zero_empty_units(const DecodeArgs& a, int worker
     const int su = u % a.S, gu = u / a.S;
     if (as_const(a.cl)[su] <= a.key_begin) {
       if (a.pre_o) {
-        // Only the shared prefix: its result is the whole result.
-        const int64_t row = (int64_t)su * a.H + gu * G;
-        for (int i = lane; i < G * D; i += 64)
-          store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
-                       a.pre_o[row * D + i], a.out_f32 != 0);
+        // Only the shared prefix: its merged chunks are the whole result.
+        constexpr int kV = G * D / 64;
+        float M, W, o[kV];
+        PrefixParts<D, G> pp;
+        pp.load(a, su, gu, lane);
+        pp.merge(M, W, o);
+        const float inv = W > 0.f ? 1.f / W : 0.f;
+        const int idx0 = lane * kV;
+#pragma unroll
+        for (int e = 0; e < kV; ++e)
+          store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + idx0 / D) * a.o_sh +
+                                  idx0 % D + e,
+                       o[e] * inv, a.out_f32 != 0);
       } else {
         for (int i = lane; i < G * D; i += 64)
           store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
@@ -269,6 +329,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   if (worker >= a.W) return;
 
   __shared__ float p_lds[kNW][kTileKeys][4];
+  __shared__ float seed_lds[kNW][G * D];  // shared-prefix seed, per wave
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kNW][G * Geo::kRowBytes];
 
   // ---- this worker's slice of the global tile list ----
@@ -381,23 +442,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 #pragma unroll
       for (int e = 0; e < kE; ++e) acc[h][e] = 0.f;
     }
-    if (a.pre_o && j0 == 0) {
-      // The unit's first piece continues the shared prefix's softmax: its
-      // state (max lse, sum 1, output o) enters once -- the sum in one lane
-      // of each 16-lane row (rows are summed at the end), the output in the
-      // lanes of V row 0 (lanes sharing a column are summed at the end).
-      const int64_t row = (int64_t)s * a.H + hq0;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        m[h] = a.pre_lse[row + h];
-        l_lane[h] = r16 == 0 ? 1.f : 0.f;
-        if (lane < Geo::kLPR) {
-#pragma unroll
-          for (int e = 0; e < kE; ++e) acc[h][e] = a.pre_o[(row + h) * D + lane * kE + e];
-        }
-      }
-    }
-
     u32x4_t kr[kDepth][Geo::kKLoads], vr[kDepth][Geo::kVLoads];
 
     auto load_tile = [&](int k, u32x4_t* kd, u32x4_t* vd) {
@@ -478,8 +522,39 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     // issues one tile's loads per computed tile (fixed waits); an epilogue
     // finishes the last 1 .. 2*kDepth-1 tiles without loading past the end.
     // The first loads are clamped to the last tile of a short partition.
+    // A unit's first piece with a shared prefix loads the prefix's chunk
+    // parts before the first K/V tiles and merges them while those are in
+    // flight.
+    const bool seed = a.pre_o && j0 == 0;
+    PrefixParts<D, G> parts;
+    if (seed) parts.load(a, s, g, lane);
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) load_tile(i, kr[i], vr[i]);
+    if (seed) {
+      // The unit's first piece continues the shared prefix's softmax: the
+      // merged state of its key chunks (max M, sum W, output) enters once --
+      // the sum in one lane of each 16-lane row (rows are summed at the
+      // end), the output in the lanes of V row 0 (lanes sharing a column
+      // are summed at the end).  The merged values reach the accumulator
+      // layout through this wave's LDS slot.
+      constexpr int kV = G * D / 64;
+      float M, W, o[kV];
+      parts.merge(M, W, o);
+#pragma unroll
+      for (int e = 0; e < kV; ++e) seed_lds[w][lane * kV + e] = o[e];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        m[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), h * D / kV));
+        const float Wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(W), h * D / kV));
+        l_lane[h] = r16 == 0 ? Wh : 0.f;
+        if (lane < Geo::kLPR) {
+#pragma unroll
+          for (int e = 0; e < kE; ++e) acc[h][e] = seed_lds[w][h * D + lane * kE + e];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int j = 0; j < kQPer; ++j)
       if (lane + 64 * j < kQChunks) *reinterpret_cast<u32x4_t*>(my_q + (lane + 64 * j) * 16) = qreg[j];
@@ -668,6 +743,7 @@ hipError_t launch_decode(const DecodePlan& pl, void* workspace, hipStream_t stre
   a.bs_shift = __builtin_ctz(pl.B);
   a.scale_log2 = pl.scale * 1.4426950408889634f;
   a.key_begin = pl.key_begin;
+  a.n_pre = pl.n_pre;
   a.pre_o = pl.pre_o;
   a.pre_lse = pl.pre_lse;
   switch (pl.dtype) {

@@ -43,9 +43,11 @@ struct DecodePlan {
   void* out = nullptr;
   int64_t o_ss = 0, o_sh = 0;
   float scale = 0.f;
-  // Shared prefix: keys [0, key_begin) were attended by the prefix step,
-  // whose merged result per (s, h) is pre_o [S, H, D] / pre_lse [S, H].
+  // Shared prefix: keys [0, key_begin) were attended by the prefix step in
+  // n_pre key chunks, whose partial results are pre_o [n_pre, H, S, D] /
+  // pre_lse [n_pre, H, S].
   int key_begin = 0;
+  int n_pre = 0;
   const float* pre_o = nullptr;
   const float* pre_lse = nullptr;
 };
@@ -71,16 +73,18 @@ struct PrefillPlan {
   int64_t o_st = 0, o_sh = 0;
   float scale = 0.f;
   // Shared-prefix attention (decode with a common prefix): one sequence given
-  // by value and key chunks writing partial results; see prefill.hip.
+  // by value and key chunks writing partial results, merged by the decode
+  // kernel; see prefill.hip.
   int fixed_L = -1, fixed_n = 0;
   int n_chunks = 1, chunk_tiles = 1 << 30;
   int64_t part_rows = 0;
   float* part_o = nullptr;
   float* part_lse = nullptr;
-  int* counters = nullptr;
-  float* merged_o = nullptr;
-  float* merged_lse = nullptr;
 };
+
+// Most key chunks the shared-prefix step splits its keys into (the decode
+// kernel merges them keeping every chunk's part in registers).
+constexpr int kMaxPrefixChunks = 4;
 
 // Query positions per prefill workgroup (all G heads of one KV head).
 constexpr int kPrefillRows = 64;

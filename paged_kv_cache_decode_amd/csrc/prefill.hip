@@ -79,26 +79,13 @@ struct PrefillArgs {
   int fixed_L, fixed_n;
   // Keys split into n_chunks chunks of chunk_tiles 64-key tiles; with
   // part_o set, each workgroup writes its normalised partial output and
-  // log2-sum-exp instead of `out`:
-  //   part_o [n_chunks, H, d, part_rows] f32, part_lse [n_chunks, H, part_rows].
+  // log2-sum-exp instead of `out`, for a later kernel to merge:
+  //   part_o [n_chunks, H, part_rows, d] f32, part_lse [n_chunks, H, part_rows].
   int n_chunks, chunk_tiles, H;
   int64_t part_rows;
   float* part_o;
   float* part_lse;
-  // With part_o set: the last of a (KV head, query tile)'s n_chunks
-  // workgroups to finish (counted in counters [Hkv * q_tiles], zero between
-  // calls) merges the chunks into merged_o [part_rows, H, d] and
-  // merged_lse [part_rows, H].
-  int* counters;
-  float* merged_o;
-  float* merged_lse;
 };
-
-// Chunk partials cross workgroups (and XCDs, whose L2 caches are not
-// coherent with each other): they are written with relaxed device-scope
-// atomic stores, which the hardware writes through to the coherent level
-// (the sc1 bit) without flushing the L2; the merging workgroup invalidates
-// its L2 once (agent-scope acquire) and then reads them with plain loads.
 
 template <class T>
 __device__ __forceinline__ f32x16_t mfma_qk(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -441,96 +428,22 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (a.part_o) {
     // Partial result of this key chunk: o / l and m + log2 l (log2 units of
-    // the scaled scores; -inf when the chunk held no visible key).  Lane
-    // (r32, hi) holds columns md*32 + 8*rg + 4*hi + 0..3 of its row.
-    const float lse = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
-    const int64_t row = q0 + my_i;
-    // Chunk partials are stored row-fastest, [chunk][H][d][rows]: the 32
-    // lanes of a store instruction (32 consecutive rows) write 128
-    // contiguous bytes, which the write-through stores need to stay whole.
-    const int64_t cbase = ((int64_t)chunk * a.H + hq) * kD;
-    if (row_ok) {
-#pragma unroll
-      for (int md = 0; md < kD / 32; ++md)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int d = md * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          __hip_atomic_store(a.part_o + (cbase + d) * a.part_rows + row, acc_o[md][r] * inv,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      if (hi == 0)
-        __hip_atomic_store(a.part_lse + ((int64_t)chunk * a.H + hq) * a.part_rows + row, lse,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // Count this chunk once every wave's stores have completed; the last
-    // chunk's workgroup merges all chunks of its rows.
-    __shared__ int last_chunk;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    int* counter = a.counters + (int64_t)g * a.q_tiles + qt;
-    if (tid == 0) {
-      const int done =
-          __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last_chunk = done == a.n_chunks - 1;
-    }
-    __syncthreads();
-    if (!last_chunk) return;
-    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // The other chunks' stores reached the coherent level before they were
-    // counted; drop this XCD's stale L2 lines once, then read them with
-    // ordinary (cached, wide) loads.
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // the scaled scores; -inf when the chunk held no visible key), row by
+    // row ([chunk][H][rows][d]; lane (r32, hi) holds columns md*32 + 8*rg +
+    // 4*hi + 0..3 of its row).  The merge happens in the next kernel on the
+    // stream, after this one's writes are complete.
     if (!row_ok) return;
-    // Log-sum-exp merge over the chunks, all read back from memory in chunk
-    // order (this chunk's own part too), so that the result does not depend
-    // on which chunk finished last: first the maximum and the weight sum,
-    // then the weighted outputs one 32-column group at a time (few registers
-    // live).
-    auto chunk_lse = [&](int c) {
-      return a.part_lse[((int64_t)c * a.H + hq) * a.part_rows + row];
-    };
-    float M = -INFINITY;
-    for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, chunk_lse(c));
-    auto weight = [&](float l) { return l == -INFINITY ? 0.f : fast_exp2(l - M); };
-    float wsum = 0.f;
-    for (int c = 0; c < a.n_chunks; ++c) wsum += weight(chunk_lse(c));
-    const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const int64_t mrow = row * a.H + hq;
-    float* mo = a.merged_o + mrow * kD;
+    const float lse = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+    const int64_t prow = ((int64_t)chunk * a.H + hq) * a.part_rows + q0 + my_i;
+    float* po = a.part_o + prow * kD;
 #pragma unroll
-    for (int md = 0; md < kD / 32; ++md) {
-      float o[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] = 0.f;
-      // Four chunks' loads in flight at a time; slots past the end read
-      // chunk 0's (valid) part with weight zero.
-      for (int c0 = 0; c0 < a.n_chunks; c0 += 4) {
-        float w[4], v[4][16];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = c0 + u;
-          const bool use = c < a.n_chunks;
-          w[u] = use ? weight(chunk_lse(c)) : 0.f;
-          const float* po =
-              a.part_o + ((int64_t)(use ? c : 0) * a.H + hq) * kD * a.part_rows + row;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            v[u][r] = po[(int64_t)(md * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)) * a.part_rows];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[r] = fmaf(w[u], v[u][r], o[r]);
-      }
+    for (int md = 0; md < kD / 32; ++md)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg)
-        *reinterpret_cast<f32x4_t*>(mo + md * 32 + 8 * rg + 4 * hi) =
-            f32x4_t{o[4 * rg] * winv, o[4 * rg + 1] * winv, o[4 * rg + 2] * winv,
-                    o[4 * rg + 3] * winv};
-    }
-    if (hi == 0) a.merged_lse[mrow] = wsum > 0.f ? M + __log2f(wsum) : -INFINITY;
+        *reinterpret_cast<f32x4_t*>(po + md * 32 + 8 * rg + 4 * hi) =
+            f32x4_t{acc_o[md][4 * rg] * inv, acc_o[md][4 * rg + 1] * inv,
+                    acc_o[md][4 * rg + 2] * inv, acc_o[md][4 * rg + 3] * inv};
+    if (hi == 0) a.part_lse[prow] = lse;
     return;
   }
   if (!row_ok) return;
@@ -612,9 +525,6 @@ hipError_t launch_prefill(const PrefillPlan& pl, hipStream_t stream) {
   a.part_rows = pl.part_rows;
   a.part_o = pl.part_o;
   a.part_lse = pl.part_lse;
-  a.counters = pl.counters;
-  a.merged_o = pl.merged_o;
-  a.merged_lse = pl.merged_lse;
   a.n_wg = (int64_t)pl.q_tiles * pl.Hkv * pl.S * pl.n_chunks;
   a.wg_per_xcd = (a.n_wg + 7) / 8;
   if (a.n_wg == 0) return hipSuccess;
