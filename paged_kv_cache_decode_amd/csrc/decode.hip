@@ -14,13 +14,15 @@
 //
 // Work decomposition (MI355X: 256 CUs, 64-lane wavefronts).  A unit is one
 // (sequence s, KV head g) pair with the G query heads that share g; it has
-// ceil(n_s / 16) tiles of 16 keys.  The tiles of all units, KV-head major
-// ((g, s) order), form one list of `total` tiles.  The kernel launches W
-// wavefronts ("workers", one workgroup of four per compute unit) and gives
-// worker i the contiguous slice [i*q, (i+1)*q) of the list,
-// q = ceil(total / W), so every worker streams the same number of bytes
-// whatever the mix of context lengths -- no tail of long partitions, no idle
-// XCD.  Worker numbers are dealt so that each of the 8 XCDs (which receive
+// ceil(n_s / 16) tiles of 16 keys.  The units, KV-head major ((g, s)
+// order), form one list in which a unit takes kUnitCost places for starting
+// it (fetching Q, refilling the load pipeline, writing its result) and then
+// one place per tile: `total` places.  The kernel launches W wavefronts
+// ("workers", one workgroup of four per compute unit) and gives worker i the
+// tiles at places [i*q, (i+1)*q) of the list, q = ceil(total / W), so every
+// worker does about the same work whatever the mix of context lengths -- no
+// tail of long partitions, no idle XCD; a worker that starts more units gets
+// fewer tiles.  Worker numbers are dealt so that each of the 8 XCDs (which receive
 // workgroups round-robin) owns one contiguous eighth of the list: with
 // head-major order an XCD then serves one or two KV heads, and K/V blocks
 // that several sequences share (a common prompt prefix) stay in its L2.
@@ -59,6 +61,14 @@ namespace {
 #define PA_DECODE_DEPTH 3
 #endif
 constexpr int kDecodeDepth = PA_DECODE_DEPTH;
+#ifndef PA_DECODE_UNIT_COST
+#define PA_DECODE_UNIT_COST 5
+#endif
+// What starting a unit costs a worker (its Q, the refilled load pipeline,
+// the partial write-out), in 16-key tiles.  Slices are equal in tiles plus
+// this cost per unit, so workers that cross many unit boundaries get fewer
+// tiles.
+constexpr int kUnitCost = PA_DECODE_UNIT_COST;
 
 template <class T, int D>
 struct DecodeGeom {
@@ -151,6 +161,9 @@ __device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
 }
 
 __device__ __forceinline__ int tiles_of(int n) { return (n + kTileKeys - 1) / kTileKeys; }
+// A unit's place in the work list: its tiles plus the start cost (none for
+// a unit without keys).
+__device__ __forceinline__ int cost_of(int n) { return n > 0 ? tiles_of(n) + kUnitCost : 0; }
 
 // Partial results cross workgroups (and XCDs, whose L2 caches are not
 // coherent with each other).  They are written and read with relaxed
@@ -337,13 +350,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   // most 64 sequences one load of the lengths serves both passes.
   // Keys this kernel attends per sequence: n_s - key_begin.
   const int lane_len = lane < a.S ? max(as_const(a.cl)[lane] - a.key_begin, 0) : 0;
-  const int lane_tiles = tiles_of(lane_len);
-  int64_t t_all = wave_sum_i64(lane_tiles);
+  const int lane_cost = cost_of(lane_len);
+  int64_t t_all = wave_sum_i64(lane_cost);
   for (int c0 = 64; c0 < a.S; c0 += 64) {
     const int s = c0 + lane;
     t_all += wave_sum_i64(
-        s < a.S ? (int64_t)tiles_of(max(as_const(a.cl)[s] - a.key_begin, 0)) : 0);
+        s < a.S ? (int64_t)cost_of(max(as_const(a.cl)[s] - a.key_begin, 0)) : 0);
   }
+  // Positions below are in cost units: a unit occupies its start cost, then
+  // one unit per tile.
   const int64_t total = t_all * a.Hkv;
   const int64_t per = (total + a.W - 1) / a.W;
   const int64_t begin = (int64_t)worker * per;
@@ -364,8 +379,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     for (int c0 = 0; c0 < a.S; c0 += 64) {
       const int ss = c0 + lane;
       const int64_t tl =
-          c0 == 0 ? lane_tiles
-                  : (ss < a.S ? (int64_t)tiles_of(max(as_const(a.cl)[ss] - a.key_begin, 0)) : 0);
+          c0 == 0 ? lane_cost
+                  : (ss < a.S ? (int64_t)cost_of(max(as_const(a.cl)[ss] - a.key_begin, 0)) : 0);
       const int64_t incl = wave_incl_scan_i64(tl, lane);
       const int64_t chunk = uniform_i64(__shfl(incl, 63));
       if (pre + chunk > r) {
@@ -393,7 +408,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 
   int64_t t = begin;
   while (t < end) {
-    // Unit (g, s) starting at list index unit_first; t lies in or after it.
+    // Unit (g, s) starting at list position unit_first (its start cost,
+    // then its tiles from tile0 on); t lies in or after it.
     // (readfirstlane marks the loop state wave-uniform for the compiler, so
     // table and length reads below become scalar loads.)
     s = uniform_i(s);
@@ -402,16 +418,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     const int n = a.S <= 64 ? __builtin_amdgcn_readlane(lane_len, s)
                             : max(as_const(a.cl)[s] - a.key_begin, 0);
     const int ts = tiles_of(n);
-    if (t >= unit_first + ts) {  // empty or finished unit: next sequence / head
-      unit_first += ts;
+    const int64_t unit_len = cost_of(n);
+    if (t >= unit_first + unit_len) {  // empty or finished unit: next sequence / head
+      unit_first += unit_len;
       if (++s == a.S) {
         s = 0;
         ++g;
       }
       continue;
     }
-    const int j0 = uniform_i((int)(t - unit_first));
-    const int j1 = uniform_i((int)min((int64_t)ts, end - unit_first));
+    const int64_t tile0 = unit_first + kUnitCost;  // list position of tile 0
+    if (tile0 >= end) break;  // the rest of this slice is the unit's start cost
+    const int j0 = uniform_i((int)(max(t, tile0) - tile0));
+    const int j1 = uniform_i((int)min((int64_t)ts, end - tile0));
     const int ntile = j1 - j0;
     const int hq0 = g * G;
 
@@ -614,8 +633,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
           store_partial(a.part_lse + (int64_t)(worker + u) * G + h, m[h] + __log2f(l_lane[h]));
       }
       // Workers first .. last hold the unit's partitions (slots worker + u).
-      const int first = (int)(unit_first / per);
-      const int last = (int)((unit_first + ts - 1) / per);
+      const int first = (int)(tile0 / per);
+      const int last = (int)((tile0 + ts - 1) / per);
       // Once this wave's partial stores have completed, count the partition;
       // the worker that brings the count to the number of partitions merges
       // them and leaves the counter at zero.
@@ -633,7 +652,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
           __hip_atomic_store(a.counters + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    t = unit_first + j1;
+    t = tile0 + j1;
   }
   zero_empty_units<T, D, G>(a, worker, lane);
 }
