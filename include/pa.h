@@ -110,9 +110,11 @@ typedef struct pa_tensor {
  *   stream       hipStream_t or NULL
  *
  * Work is balanced over a fixed set of W wavefronts (one workgroup of four
- * per compute unit, W = 1024 on an MI355X): the 16-key tiles of all (sequence, KV head) pairs form one list
- * that is cut into W equal contiguous slices, so long contexts are split
- * into partitions processed in parallel and joined by a log-sum-exp merge.
+ * per compute unit, W = 1024 on an MI355X): the 16-key tiles of all
+ * (sequence, KV head) pairs form one list, in which each pair also counts a
+ * fixed start cost, cut into W contiguous slices of equal cost.  Long
+ * contexts are so split into partitions processed in parallel and joined by
+ * a log-sum-exp merge.
  * A wavefront that finishes the last partition of a split (sequence, KV
  * head) pair merges that pair's partitions itself: one kernel per call.
  *
