@@ -34,12 +34,42 @@ def out_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def assert_close_f32_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+def assert_close_f32_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "",
+                         factor: float = 1.0):
+    """Max-abs check against TOL[dtype] * factor (factor > 1 only for scores
+    larger than the standard scale gives; see score_factor)."""
+    tol = TOL[dtype] * factor
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     worst = float(err.max()) if err.size else 0.0
-    assert worst <= TOL[dtype], f"{what}: max-abs error {worst:.3e} > {TOL[dtype]:.1e}"
+    assert worst <= tol, f"{what}: max-abs error {worst:.3e} > {tol:.1e}"
     return worst
+
+
+def score_factor(c) -> float:
+    """How far a decode case's scaled scores exceed the standard range.
+
+    The kernels compute the scores s * scale in fp32, so their rounding error
+    grows with |s * scale|; the tolerances above hold for the standard
+    1/sqrt(d) scale on unit-normal data, where |s * scale| stays below about
+    4.  This returns max(1, X / 4), X = the largest |s * scale| over the
+    case's attended keys (computed in fp64 from the stored inputs)."""
+    from oracle.dtypes import to_f64
+    q = to_f64(c.q, c.dtype)
+    k = to_f64(c.k_pool, c.dtype)
+    S, H, _ = q.shape
+    Hkv, B = k.shape[2], k.shape[1]
+    G = H // Hkv
+    x_max = 0.0
+    for s in range(S):
+        n = int(c.context_lens[s])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        rows = k[c.block_table[s, t // B].astype(np.int64), t % B]  # [n, Hkv, d]
+        for h in range(H):
+            x_max = max(x_max, float(np.abs(rows[:, h // G] @ q[s, h]).max()) * abs(c.scale))
+    return max(1.0, x_max / 4.0)
 
 
 def assert_close_native_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
