@@ -37,7 +37,7 @@
  *     Logical token t of sequence s lives in physical block
  *     block_table[s][t / B], slot t % B.  Query head h reads KV head h / G.
  *   - Supported instances: dtype f32, f16 or bf16 (prefill: f16, bf16);
- *     d in {64, 128} (prefill: 128); B in {16, 32, 64, 128}; G in {1, 2, 4}.
+ *     d in {64, 128} (prefill: 128); B in {16, 32, 64, 128}; G in {1, 2, 4, 8}.
  *     Other shapes return PA_ERR_UNSUPPORTED.
  *   - Device-side contents the host cannot check without a synchronisation
  *     are the caller's contract: 0 <= n_s <= MB * B; block_table[s][j] in

@@ -341,7 +341,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   const int worker = logical * kNW + w;
   if (worker >= a.W) return;
 
-  __shared__ float p_lds[kNW][kTileKeys][4];
+  __shared__ float p_lds[kNW][kTileKeys][G > 4 ? G : 4];
   __shared__ float seed_lds[kNW][G * D];  // shared-prefix seed, per wave
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kNW][G * Geo::kRowBytes];
 
@@ -404,7 +404,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   const uint32_t k_off = (uint32_t)r16 * tok_stride + c * 16;
   const uint32_t v_off = (uint32_t)v_row * tok_stride + (lane % Geo::kLPR) * 16;
   uint8_t* my_q = q_lds[w];
-  const uint8_t* q_frag = my_q + (r16 % G) * Geo::kRowBytes + c * 16;
+  // Q as the MFMA A operand: its 16 rows repeat the heads of a chain.  Up to
+  // 4 heads fit one 16x16 product (a lane's 4 results are heads 0..3); a
+  // group of 8 takes two chains (heads 0..3 and 4..7) on the same K.
+  constexpr int kChains = (G + 3) / 4;
+  constexpr int kHC = G / kChains;  // heads per chain
+  const uint8_t* q_frag = my_q + (r16 % kHC) * Geo::kRowBytes + c * 16;
 
   int64_t t = begin;
   while (t < end) {
@@ -482,18 +487,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 
     auto compute_tile = [&](int k, const u32x4_t* kf, const u32x4_t* vf) {
       const int valid = n - (j0 + k) * kTileKeys;  // keys of this tile below n (>= 1)
-      u32x4_t qf[Geo::kKLoads];
+      f32x4_t sc[kChains];
 #pragma unroll
-      for (int i = 0; i < Geo::kKLoads; ++i)
-        qf[i] = *reinterpret_cast<const u32x4_t*>(q_frag + i * 64);
-      const f32x4_t sc = qk_tile<T, D>(qf, kf);
+      for (int ch = 0; ch < kChains; ++ch) {
+        u32x4_t qf[Geo::kKLoads];
+#pragma unroll
+        for (int i = 0; i < Geo::kKLoads; ++i)
+          qf[i] = *reinterpret_cast<const u32x4_t*>(q_frag + ch * kHC * Geo::kRowBytes + i * 64);
+        sc[ch] = qk_tile<T, D>(qf, kf);
+      }
       const bool key_ok = r16 < valid;
       float x[G], pr[G], mnew[G];
       bool grow = false;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         // Slots at or past n are selected away (they may hold NaN).
-        x[h] = key_ok ? sc[h] * a.scale_log2 : -INFINITY;
+        x[h] = key_ok ? sc[h / kHC][h % kHC] * a.scale_log2 : -INFINITY;
         const float tmax = uniform(row16_max(x[h]));
         mnew[h] = fmaxf(m[h], tmax);
         grow |= mnew[h] > m[h];
@@ -686,9 +695,11 @@ int resident_waves_shape(int D, int G) {
     case 641: return resident_waves_t<T, 64, 1>();
     case 642: return resident_waves_t<T, 64, 2>();
     case 644: return resident_waves_t<T, 64, 4>();
+    case 648: return resident_waves_t<T, 64, 8>();
     case 1281: return resident_waves_t<T, 128, 1>();
     case 1282: return resident_waves_t<T, 128, 2>();
     case 1284: return resident_waves_t<T, 128, 4>();
+    case 1288: return resident_waves_t<T, 128, 8>();
     default: return 0;
   }
 }
@@ -699,9 +710,11 @@ hipError_t dispatch_shape(const DecodePlan& pl, const DecodeArgs& a, hipStream_t
     case 641: return launch_decode_t<T, 64, 1>(pl, a, stream);
     case 642: return launch_decode_t<T, 64, 2>(pl, a, stream);
     case 644: return launch_decode_t<T, 64, 4>(pl, a, stream);
+    case 648: return launch_decode_t<T, 64, 8>(pl, a, stream);
     case 1281: return launch_decode_t<T, 128, 1>(pl, a, stream);
     case 1282: return launch_decode_t<T, 128, 2>(pl, a, stream);
     case 1284: return launch_decode_t<T, 128, 4>(pl, a, stream);
+    case 1288: return launch_decode_t<T, 128, 8>(pl, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -78,7 +78,7 @@ bool is_float(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
 
 bool supported_block(int64_t B) { return B == 16 || B == 32 || B == 64 || B == 128; }
 
-bool supported_group(int64_t G) { return G == 1 || G == 2 || G == 4; }
+bool supported_group(int64_t G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 
 // Pools: [NB, B, Hkv, d], contiguous, same shape and dtype for K and V.
 int check_pools(const pa_tensor* k, const pa_tensor* v, std::string* err) {
@@ -194,7 +194,7 @@ int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_
     return fail(err, PA_ERR_UNSUPPORTED, "block size %lld not compiled (16/32/64/128)",
                 (long long)B);
   if (!supported_group(G))
-    return fail(err, PA_ERR_UNSUPPORTED, "group size H/Hkv = %lld not compiled (1/2/4)",
+    return fail(err, PA_ERR_UNSUPPORTED, "group size H/Hkv = %lld not compiled (1/2/4/8)",
                 (long long)G);
   const int64_t MB = block_table->shape[1];
   if (S > 0 && MB < 1) return fail(err, PA_ERR_SHAPE, "block_table has no columns");
@@ -290,7 +290,7 @@ int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v
     return fail(err, PA_ERR_UNSUPPORTED, "block size %lld not compiled (16/32/64/128)",
                 (long long)B);
   if (!supported_group(G))
-    return fail(err, PA_ERR_UNSUPPORTED, "group size H/Hkv = %lld not compiled (1/2/4)",
+    return fail(err, PA_ERR_UNSUPPORTED, "group size H/Hkv = %lld not compiled (1/2/4/8)",
                 (long long)G);
   const int64_t MB = block_table->shape[1];
   if (S > 0 && MB < 1) return fail(err, PA_ERR_SHAPE, "block_table has no columns");
@@ -306,10 +306,12 @@ int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v
   p.max_query_len = max_query_len;
   p.causal = causal;
   p.q_tiles = (max_query_len + kPrefillRows - 1) / kPrefillRows;
-  p.grid[0] = (int64_t)p.q_tiles * Hkv * S;
+  // Groups of 8 heads run as two workgroups of 4 heads per KV head.
+  const int64_t kv_div = G > 4 ? G / 4 : 1;
+  p.grid[0] = (int64_t)p.q_tiles * Hkv * kv_div * S;
   p.grid[1] = 1;
   p.grid[2] = 1;
-  p.block_threads = 64 * kPrefillRowWaves * (int)G;  // 32 positions of one head per wave
+  p.block_threads = 64 * kPrefillRowWaves * (int)(G / kv_div);  // 32 positions of one head per wave
   p.q = q->data; p.q_st = q->stride[0]; p.q_sh = q->stride[1];
   p.k = k_pool->data; p.v = v_pool->data;
   p.bt = static_cast<const int32_t*>(block_table->data); p.bt_ss = block_table->stride[0];

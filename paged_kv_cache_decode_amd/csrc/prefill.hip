@@ -71,7 +71,11 @@ struct PrefillArgs {
   int out_f32;
   int S, Hkv, MB, q_tiles, bs_shift, causal;
   uint32_t q_sign;     // XORed into Q's 16-bit lanes (0x80008000 when scale < 0)
-  int64_t n_wg;        // real workgroups (q_tiles * Hkv * S * n_chunks)
+  // Head groups of more than 4 heads run as kv_div workgroups of 4 heads per
+  // KV head (each reads that KV head's K/V): workgroup group g covers query
+  // heads 4g .. 4g+3 and KV head g / kv_div.  kv_div = 1 otherwise.
+  int kv_div;
+  int64_t n_wg;        // real workgroups (q_tiles * Hkv * kv_div * S * n_chunks)
   int64_t wg_per_xcd;  // ceil(n_wg / 8)
   float c;             // |scale| * log2(e)
   // One sequence given by value (fixed_L >= 0): L = fixed_L rows, n =
@@ -208,8 +212,8 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   const int tok_stride = a.Hkv * kD * 2;  // bytes between consecutive slots
   const int bmask = (1 << a.bs_shift) - 1;
   const int64_t block_bytes = (int64_t)tok_stride << a.bs_shift;
-  const uint8_t* kbase = a.k + (int64_t)g * kD * 2;
-  const uint8_t* vbase = a.v + (int64_t)g * kD * 2;
+  const uint8_t* kbase = a.k + (int64_t)(g / a.kv_div) * kD * 2;
+  const uint8_t* vbase = a.v + (int64_t)(g / a.kv_div) * kD * 2;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index (uniform)
   // Gather addressing.  Every load instruction of a wave covers 4 (K) or 8
   // (V) consecutive keys starting at a multiple of 4 (8), so all its lanes
@@ -485,7 +489,8 @@ hipError_t dispatch_group(const PrefillPlan& pl, const PrefillArgs& a, hipStream
   switch (pl.G) {
     case 1: return launch_prefill_t<T, 1>(a, stream);
     case 2: return launch_prefill_t<T, 2>(a, stream);
-    case 4: return launch_prefill_t<T, 4>(a, stream);
+    case 4:
+    case 8: return launch_prefill_t<T, 4>(a, stream);  // 8: two workgroups per KV head
     default: return hipErrorInvalidValue;
   }
 }
@@ -525,7 +530,8 @@ hipError_t launch_prefill(const PrefillPlan& pl, hipStream_t stream) {
   a.part_rows = pl.part_rows;
   a.part_o = pl.part_o;
   a.part_lse = pl.part_lse;
-  a.n_wg = (int64_t)pl.q_tiles * pl.Hkv * pl.S * pl.n_chunks;
+  a.kv_div = pl.G > 4 ? pl.G / 4 : 1;
+  a.n_wg = (int64_t)pl.q_tiles * pl.Hkv * a.kv_div * pl.S * pl.n_chunks;
   a.wg_per_xcd = (a.n_wg + 7) / 8;
   if (a.n_wg == 0) return hipSuccess;
   switch (pl.dtype) {

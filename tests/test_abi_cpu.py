@@ -105,7 +105,7 @@ def test_status_strings():
     (lambda a: a["q"].stride.__setitem__(2, 2), -4),
     (lambda a: a.update(decode_args(d=96)), -5),
     (lambda a: a.update(decode_args(Bs=8)), -5),
-    (lambda a: a.update(decode_args(Hkv=4)), -5),
+    (lambda a: a.update(decode_args(Hkv=2)), -5),  # G = 16
     (lambda a: a.update(decode_args(H=24, Hkv=8)), -5),
     (lambda a: setattr(a["out"], "data", 2 * GAP + 4096), -8),
 ])

@@ -48,7 +48,7 @@ EDGE_LENS = [0, 1, 15, 16, 17, 63, 64, 65, 100, 257, 1000, 1537]
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("G", [1, 2, 4])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_decode_shapes(pa, dtype, d, G):
     Hkv = 2
     c = W.make_decode_case(100 + d + G, len(EDGE_LENS), G * Hkv, Hkv, d, 16, dtype,

@@ -36,7 +36,7 @@ def oracle_prefill(c):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("G", [1, 2, 4])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_small(pa, dtype, G, causal):
     lens = [1, 63, 64, 65, 200, 130]

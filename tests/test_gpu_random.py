@@ -40,7 +40,7 @@ def test_decode_random_configs(pa, monkeypatch, seed):
     rng = np.random.default_rng(5000 + seed)
     dtype = str(rng.choice(["f32", "f16", "bf16"]))
     d = int(rng.choice([64, 128]))
-    G = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
     B = int(rng.choice([16, 32, 64, 128]))
     S = int(rng.integers(1, 100))
@@ -73,7 +73,7 @@ def test_decode_random_configs(pa, monkeypatch, seed):
 def test_prefill_random_configs(pa, seed):
     rng = np.random.default_rng(7000 + seed)
     dtype = str(rng.choice(["f16", "bf16"]))
-    G = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
     Hkv = int(rng.choice([1, 2, 4]))
     B = int(rng.choice([16, 32, 64, 128]))
     S = int(rng.integers(1, 7))
@@ -105,7 +105,7 @@ def test_prefill_random_configs(pa, seed):
 def test_shared_prefix_random_configs(pa, seed):
     rng = np.random.default_rng(9000 + seed)
     B = int(rng.choice([16, 32, 64, 128]))
-    G = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
     Hkv = int(rng.choice([1, 2, 4]))
     S = int(rng.integers(1, 90))
     prefix_len = B * int(rng.integers(1, 40))

@@ -61,7 +61,7 @@ def test_shared_prefix_only_and_empty_suffixes(pa):
     assert_close_f32_out(got, oracle_all(c), "bf16", "prefix only")
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 4), (4, 2)])
+@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 4), (4, 2), (8, 2)])
 def test_shared_prefix_group_sizes(pa, G, Hkv):
     c = W.make_prefix_shared_case(720 + G, 16, num_seqs=70, prefix_len=192,
                                   suffix_range=(1, 130), num_heads=G * Hkv, num_kv_heads=Hkv,
