@@ -44,8 +44,10 @@
 //   * loads the V rows with full-row coalescing (16 lanes x 16 bytes per
 //     256-byte row) and accumulates p * v in fp32 on the VALU, reading the
 //     probabilities of its key from a 256-byte per-wave LDS slot.
-// Three register sets rotate so that two tiles are in flight while the third
-// is being used (about 5 us of loaded memory latency has to be covered).
+// Two register sets rotate: one tile's loads are in flight while the other
+// tile is used.  (Three sets, two tiles in flight, measured slower once the
+// slices account for unit starts: a shallower pipeline refills faster at a
+// unit boundary, and 4 waves x 2 tiles x 8 KiB per CU still keep HBM busy.)
 #include "device_common.h"
 #include "kernels.h"
 #include "launch.h"
@@ -58,7 +60,7 @@ namespace pa {
 namespace {
 
 #ifndef PA_DECODE_DEPTH
-#define PA_DECODE_DEPTH 3
+#define PA_DECODE_DEPTH 2
 #endif
 constexpr int kDecodeDepth = PA_DECODE_DEPTH;
 #ifndef PA_DECODE_UNIT_COST
@@ -673,9 +675,9 @@ hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
 }
 
 // One workgroup (kDecodeWaves wavefronts) per compute unit.  Measured on
-// MI355X, one wavefront per SIMD with three tiles in flight streams K/V
-// faster than two: fewer, longer slices mean fewer pipeline restarts at unit
-// boundaries and fewer partitions, with enough bytes still in flight.
+// MI355X, one wavefront per SIMD streams K/V faster than two: fewer, longer
+// slices mean fewer pipeline restarts at unit boundaries and fewer
+// partitions, with enough bytes still in flight.
 template <class T, int D, int G>
 int resident_waves_t() {
   int dev = 0, cus = 0, per_cu = 0;
