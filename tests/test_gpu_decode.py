@@ -88,6 +88,17 @@ def test_decode_worker_count_invariance(pa, monkeypatch, workers):
     assert np.abs(got - one).max() <= 1e-5
 
 
+def test_decode_many_sequences(pa):
+    """1,500 short sequences (lengths 0 .. 200): thousands of units, most
+    workers crossing many unit boundaries, the lengths read from memory
+    rather than from one register of 64."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(0, 201, size=1500)]
+    c = W.make_decode_case(770, 1500, 8, 2, 128, 16, "bf16", lens=lens)
+    got = out_to_f64(run_decode(pa, c))
+    assert_close_f32_out(got, oracle_decode(c), "bf16", "1500 sequences")
+
+
 def test_decode_is_deterministic(pa):
     c = W.make_decode_case(301, 8, 32, 8, 128, 16, "bf16", len_range=(1, 3000))
     dev = case_to_dev(c)
