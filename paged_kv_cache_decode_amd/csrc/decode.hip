@@ -36,7 +36,9 @@
 // Per 16-key tile a worker:
 //   * loads the K rows with the lane layout of the 16x16 MFMA B operand
 //     (lane = key r16 and 16-byte column group c): every load instruction
-//     reads 64 contiguous bytes of each of 16 rows;
+//     reads 64 contiguous bytes of each of 16 rows (or, in the suffix step
+//     after a shared prefix, whole rows like V, moved into that layout
+//     through LDS);
 //   * computes S = Q K^T on one MFMA chain; Q (the A operand) repeats the G
 //     heads down its 16 rows, so every lane ends with the scores of its key
 //     for all G heads (no transposes, no cross-lane traffic);
@@ -327,7 +329,13 @@ __device__ __forceinline__ void zero_empty_units(const DecodeArgs& a, int worker
   }
 }
 
-template <class T, int D, int G>
+// kKRows selects how K is read.  false: in the MFMA operand layout, 64
+// bytes of 16 rows per load instruction, with normal caching.  true: whole
+// rows per instruction like V, non-temporal, then moved into the operand
+// layout through this wave's LDS slot (used for the suffix step after a
+// shared prefix, where it measured faster; plain decode measured slower
+// with it).
+template <class T, int D, int G, bool kKRows>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(DecodeArgs a) {
   using Geo = DecodeGeom<T, D>;
   constexpr int kDepth = kDecodeDepth;  // tiles whose loads are in flight per wave
@@ -346,6 +354,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   __shared__ float p_lds[kNW][kTileKeys][G > 4 ? G : 4];
   __shared__ float seed_lds[kNW][G * D];  // shared-prefix seed, per wave
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kNW][G * Geo::kRowBytes];
+  // K tile in the MFMA operand layout (kKRows): rows padded by 16 bytes, so
+  // that the 16 rows one read instruction covers start on different banks.
+  constexpr int kKPad = Geo::kRowBytes + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kNW][kKRows ? kTileKeys * kKPad : 16];
 
   // ---- this worker's slice of the global tile list ----
   // Tiles per KV head over all sequences (the list is g-major).  With at
@@ -468,6 +480,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 #pragma unroll
       for (int e = 0; e < kE; ++e) acc[h][e] = 0.f;
     }
+    static_assert(Geo::kKLoads == Geo::kVLoads, "a K row and a V row take the same loads");
     u32x4_t kr[kDepth][Geo::kKLoads], vr[kDepth][Geo::kVLoads];
 
     auto load_tile = [&](int k, u32x4_t* kd, u32x4_t* vd) {
@@ -476,12 +489,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
       const int64_t row0 = (int64_t)phys * blk_stride + (int64_t)(key0 & bmask) * tok_stride;
       const uint8_t* kb = kbase + row0;
       const uint8_t* vb = vbase + row0;
+      if constexpr (kKRows) {
 #pragma unroll
-      for (int i = 0; i < Geo::kKLoads; ++i) kd[i] = load16(kb + k_off + i * 64);
+        for (int i = 0; i < Geo::kVLoads; ++i)
+          kd[i] = load16_stream(kb + (int64_t)(i * Geo::kRPI) * tok_stride + v_off);
+      } else {
+#pragma unroll
+        for (int i = 0; i < Geo::kKLoads; ++i) kd[i] = load16(kb + k_off + i * 64);
+      }
       // V rows are read whole by one instruction each: non-temporal, so
       // streaming V does not push reusable lines out of the caches.  K rows
-      // are read 64 bytes at a time by four instructions, and the second
-      // half of each 128-byte line must still be in L2 when it is needed.
+      // in the operand layout are read 64 bytes at a time by four
+      // instructions, and the second half of each 128-byte line must still be
+      // in L2 when it is needed, so they keep normal caching.
 #pragma unroll
       for (int i = 0; i < Geo::kVLoads; ++i)
         vd[i] = load16_stream(vb + (int64_t)(i * Geo::kRPI) * tok_stride + v_off);
@@ -489,6 +509,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 
     auto compute_tile = [&](int k, const u32x4_t* kf, const u32x4_t* vf) {
       const int valid = n - (j0 + k) * kTileKeys;  // keys of this tile below n (>= 1)
+      u32x4_t kq[Geo::kKLoads];
+      if constexpr (kKRows) {
+        // Whole rows -> LDS -> operand layout (row r16, bytes i*64 + c*16).
+        uint8_t* kl = k_lds[w];
+#pragma unroll
+        for (int i = 0; i < Geo::kVLoads; ++i)
+          *reinterpret_cast<u32x4_t*>(kl + (i * Geo::kRPI + v_row) * kKPad +
+                                      (lane % Geo::kLPR) * 16) = kf[i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < Geo::kKLoads; ++i)
+          kq[i] = *reinterpret_cast<const u32x4_t*>(kl + r16 * kKPad + i * 64 + c * 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < Geo::kKLoads; ++i) kq[i] = kf[i];
+      }
       f32x4_t sc[kChains];
 #pragma unroll
       for (int ch = 0; ch < kChains; ++ch) {
@@ -496,7 +532,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 #pragma unroll
         for (int i = 0; i < Geo::kKLoads; ++i)
           qf[i] = *reinterpret_cast<const u32x4_t*>(q_frag + ch * kHC * Geo::kRowBytes + i * 64);
-        sc[ch] = qk_tile<T, D>(qf, kf);
+        sc[ch] = qk_tile<T, D>(qf, kq);
       }
       const bool key_ok = r16 < valid;
       float x[G], pr[G], mnew[G];
@@ -670,7 +706,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 
 template <class T, int D, int G>
 hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t stream) {
-  return timed_launch("decode_partitions", decode_partitions_kernel<T, D, G>,
+  // The suffix step after a shared prefix (fp16 / bf16, d = 128 only) reads
+  // K as whole rows.
+  if constexpr (D == 128 && !__is_same(T, TF32)) {
+    if (pl.pre_o)
+      return timed_launch("decode_partitions", decode_partitions_kernel<T, D, G, true>,
+                          dim3((unsigned)pl.grid[0]), dim3(pl.block_threads), stream, a);
+  }
+  return timed_launch("decode_partitions", decode_partitions_kernel<T, D, G, false>,
                       dim3((unsigned)pl.grid[0]), dim3(pl.block_threads), stream, a);
 }
 
@@ -685,7 +728,7 @@ int resident_waves_t() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(decode_partitions_kernel<T, D, G>),
+          &per_cu, reinterpret_cast<const void*>(decode_partitions_kernel<T, D, G, false>),
           64 * kDecodeWaves, 0) != hipSuccess)
     return 0;
   return per_cu >= 1 ? cus * kDecodeWaves : 0;

@@ -95,6 +95,29 @@ def test_causal_bf16_prefill_sampled(pa):
         assert_close_f32_out(got[t, h], ref[r], "bf16", f"row {t} head {h}")
 
 
+def test_prefill_many_prompts(pa):
+    """90 prompts, mostly short (the padded grid then holds far more empty
+    query-tile slots than real ones), some continuing a longer context:
+    sampled rows, including every prompt's first and last row."""
+    rng = np.random.default_rng(430)
+    S = 90
+    lens = [int(x) for x in rng.integers(1, 300, size=S)]
+    lens[7], lens[50] = 1500, 900
+    qlens = [n if rng.random() < 0.7 else int(rng.integers(1, n + 1)) for n in lens]
+    c = W.make_prefill_case(431, S, 8, 2, 128, 16, "bf16", lens=lens, query_lens=qlens,
+                            causal=True)
+    got = out_to_f64(run_prefill(pa, c))
+    qsl = c.query_start_loc
+    rows = []
+    for s in range(S):
+        for t in {int(qsl[s]), int(qsl[s + 1] - 1), int(rng.integers(qsl[s], qsl[s + 1]))}:
+            rows.append((t, int(rng.integers(0, 8))))
+    ref, _ = oracle.prefill_rows(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, qsl,
+                                 c.scale, True, c.dtype, rows)
+    sel = np.stack([got[t, h] for t, h in rows])
+    assert_close_f32_out(sel, ref, "bf16", "90 prompts")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_write_kv_bit_exact(pa, dtype):
     rng = np.random.default_rng(5)
