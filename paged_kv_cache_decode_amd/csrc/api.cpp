@@ -292,7 +292,10 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   pp.NB = plan.NB;
   pp.max_query_len = plan.S;
   pp.causal = 0;
-  pp.q_tiles = (plan.S + pa::kPrefillRows - 1) / pa::kPrefillRows;
+  // Workgroups of 32 query rows: the S rows are few, and smaller workgroups
+  // spread them over twice as many CUs.
+  pp.row_waves = 1;
+  pp.q_tiles = (plan.S + 31) / 32;
   pp.q = plan.q;
   pp.q_st = plan.q_ss;
   pp.q_sh = plan.q_sh;

@@ -311,7 +311,7 @@ int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v
   p.grid[0] = (int64_t)p.q_tiles * Hkv * kv_div * S;
   p.grid[1] = 1;
   p.grid[2] = 1;
-  p.block_threads = 64 * kPrefillRowWaves * (int)(G / kv_div);  // 32 positions of one head per wave
+  p.block_threads = 64 * p.row_waves * (int)(G / kv_div);  // 32 positions of one head per wave
   p.q = q->data; p.q_st = q->stride[0]; p.q_sh = q->stride[1];
   p.k = k_pool->data; p.v = v_pool->data;
   p.bt = static_cast<const int32_t*>(block_table->data); p.bt_ss = block_table->stride[0];

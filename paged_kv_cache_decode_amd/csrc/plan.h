@@ -52,13 +52,19 @@ struct DecodePlan {
   const float* pre_lse = nullptr;
 };
 
+// Query positions per prefill workgroup (all G heads of one KV head).
+constexpr int kPrefillRows = 64;
+// Waves per query head in a prefill workgroup (each wave owns 32 positions).
+constexpr int kPrefillRowWaves = kPrefillRows / 32;
+
 struct PrefillPlan {
   int dtype = 0, out_dtype = 0;
   int S = 0, T = 0, H = 0, Hkv = 0, G = 0, D = 0, B = 0, MB = 0;
   int64_t NB = 0;
   int max_query_len = 0;
   int causal = 0;
-  int q_tiles = 0;  // ceil(max_query_len / kPrefillRows)
+  int row_waves = kPrefillRowWaves;  // waves per head: 32 * row_waves query rows per workgroup
+  int q_tiles = 0;  // ceil(max_query_len / (32 * row_waves))
   int64_t grid[3] = {0, 0, 0};
   int block_threads = 0;
   const void* q = nullptr;
@@ -85,11 +91,6 @@ struct PrefillPlan {
 // Most key chunks the shared-prefix step splits its keys into (the decode
 // kernel merges them keeping every chunk's part in registers).
 constexpr int kMaxPrefixChunks = 4;
-
-// Query positions per prefill workgroup (all G heads of one KV head).
-constexpr int kPrefillRows = 64;
-// Waves per query head in a prefill workgroup (each wave owns 32 positions).
-constexpr int kPrefillRowWaves = kPrefillRows / 32;
 
 struct WriteKvPlan {
   int dtype = 0;

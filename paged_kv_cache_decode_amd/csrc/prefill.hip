@@ -9,7 +9,8 @@
 // skipped).
 //
 // Work decomposition:
-//   workgroup = kPrefillRows query positions x the G query heads of one KV
+//   workgroup = 32 * RW query positions (64 for packed prompts, 32 for the
+//   shared-prefix step) x the G query heads of one KV
 //   head (a wave owns 32 positions of one head).  K/V tiles of 64 keys
 //   are gathered once per workgroup into LDS and feed all G heads.  Key
 //   tiles wholly above the diagonal are never loaded.  LDS is double
@@ -139,9 +140,11 @@ __device__ __forceinline__ float swap_halves(float x) {
 // adjacent); it spreads the transposing writes over the LDS banks.
 __device__ __forceinline__ int vt_col(int d, int kp) { return kp ^ ((d >> 5) << 1); }
 
-template <class T, int G>
-__global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(PrefillArgs a) {
-  constexpr int kNT = 64 * kPrefillRowWaves * G;  // threads
+// RW waves per head: a workgroup covers 32 * RW query positions.
+template <class T, int G, int RW>
+__global__ __launch_bounds__(64 * RW * G) void prefill_kernel(PrefillArgs a) {
+  constexpr int kNT = 64 * RW * G;  // threads
+  constexpr int kRows = 32 * RW;    // query positions per workgroup
   constexpr int kKPer = kKChunks / kNT;
   constexpr int kVPer = kVUnits / kNT;
   static_assert(kKPer * kNT == kKChunks && kVPer * kNT == kVUnits, "tile split");
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   const int q0 = a.fixed_L >= 0 ? 0 : qsl[s];
   const int L = a.fixed_L >= 0 ? a.fixed_L : qsl[s + 1] - q0;
   const int n = a.fixed_L >= 0 ? a.fixed_n : as_const(a.cl)[s];
-  if (qt * kPrefillRows >= L) return;
+  if (qt * kRows >= L) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,14 +181,14 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
   const int hi = lane >> 5;
 
   // This wave's rows: i = row0 + r32 (query index within the sequence).
-  const int row0 = qt * kPrefillRows + half * 32;
+  const int row0 = qt * kRows + half * 32;
   const int my_i = row0 + r32;
   const bool row_ok = my_i < L;
   const int shift = n - L;  // absolute position of row i is shift + i
 
   // Keys the workgroup needs: [0, kend).
   int kend = n;
-  if (a.causal) kend = min(n, shift + min(qt * kPrefillRows + kPrefillRows, L));
+  if (a.causal) kend = min(n, shift + min(qt * kRows + kRows, L));
   const int ntk = (kend + kBN - 1) / kBN;
   // Per wave: tiles below `full` need no mask; tiles from `full` up to
   // `last` need one; later tiles hold no visible key for this wave.
@@ -477,20 +480,29 @@ __global__ __launch_bounds__(64 * kPrefillRowWaves * G) void prefill_kernel(Pref
     }
 }
 
-template <class T, int G>
+template <class T, int G, int RW>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = a.wg_per_xcd * 8;
-  return timed_launch("prefill", prefill_kernel<T, G>, dim3((unsigned)blocks),
-                      dim3(64 * kPrefillRowWaves * G), stream, a);
+  return timed_launch("prefill", prefill_kernel<T, G, RW>, dim3((unsigned)blocks),
+                      dim3(64 * RW * G), stream, a);
+}
+
+template <class T, int RW>
+hipError_t dispatch_group(const PrefillPlan& pl, const PrefillArgs& a, hipStream_t stream) {
+  switch (pl.G) {
+    case 1: return launch_prefill_t<T, 1, RW>(a, stream);
+    case 2: return launch_prefill_t<T, 2, RW>(a, stream);
+    case 4:
+    case 8: return launch_prefill_t<T, 4, RW>(a, stream);  // 8: two workgroups per KV head
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <class T>
-hipError_t dispatch_group(const PrefillPlan& pl, const PrefillArgs& a, hipStream_t stream) {
-  switch (pl.G) {
-    case 1: return launch_prefill_t<T, 1>(a, stream);
-    case 2: return launch_prefill_t<T, 2>(a, stream);
-    case 4:
-    case 8: return launch_prefill_t<T, 4>(a, stream);  // 8: two workgroups per KV head
+hipError_t dispatch_rows(const PrefillPlan& pl, const PrefillArgs& a, hipStream_t stream) {
+  switch (pl.row_waves) {
+    case 1: return dispatch_group<T, 1>(pl, a, stream);
+    case 2: return dispatch_group<T, 2>(pl, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -535,8 +547,8 @@ hipError_t launch_prefill(const PrefillPlan& pl, hipStream_t stream) {
   a.wg_per_xcd = (a.n_wg + 7) / 8;
   if (a.n_wg == 0) return hipSuccess;
   switch (pl.dtype) {
-    case PA_F16: return dispatch_group<TF16>(pl, a, stream);
-    case PA_BF16: return dispatch_group<TBF16>(pl, a, stream);
+    case PA_F16: return dispatch_rows<TF16>(pl, a, stream);
+    case PA_BF16: return dispatch_rows<TBF16>(pl, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
