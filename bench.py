@@ -61,7 +61,8 @@ def parse():
                          "profiles/<KERNEL>_<WORKLOAD>_traffic.json (no GPU needed)")
     ap.add_argument("--only", default="",
                     help="comma list of workloads to run (for profiling): "
-                         "gqa,long,prefix,prefill")
+                         "gqa,long,prefix,prefill; prefix16 runs the prefix-shared "
+                         "workload at B = 16 only")
     return ap.parse_args()
 
 
@@ -88,9 +89,17 @@ def load_traffic(kernel, workload, src_hash, bytes_per_launch):
             "scale_factor": rec.get("scale_factor"), "source": os.path.basename(path)}
 
 
-# Kernel (as the library's timer names it) -> (substring of its symbol, source).
+# Kernel record name -> (substring of its demangled symbol, source).  The
+# last three tell apart the kernels of the prefix-shared workload: plain
+# decode, and the shared-prefix call's prefix step (32-row prefill) and
+# suffix step (whole-row K).
 KERNEL_SOURCES = {"decode_partitions": ("decode_partitions_kernel", "decode.hip"),
-                  "prefill": ("prefill_kernel", "prefill.hip")}
+                  "prefill": ("prefill_kernel", "prefill.hip"),
+                  "decode_partitions_plain":
+                      ("decode_partitions_kernel<pa::TBF16, 128, 4, false>", "decode.hip"),
+                  "decode_partitions_suffix":
+                      ("decode_partitions_kernel<pa::TBF16, 128, 4, true>", "decode.hip"),
+                  "prefill_prefix": ("prefill_kernel<pa::TBF16, 4, 1>", "prefill.hip")}
 COPY_CALIBRATION_BYTES = 1 << 30
 
 
@@ -131,6 +140,32 @@ def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_w
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+
+
+def prefix_dram_measured(unique):
+    """Measured DRAM bytes per call on the prefix-shared workload at B = 16
+    (rocprofv3 counter records, if taken on the current sources), against
+    the unique bytes the method must move."""
+    wl = "prefix-shared-bf16-decode-B16"
+    dec, pre = source_hash("decode.hip"), source_hash("prefill.hip")
+    plain = load_traffic("decode_partitions_plain", wl, dec, unique)
+    prefix = load_traffic("prefill_prefix", wl, pre, unique)
+    suffix = load_traffic("decode_partitions_suffix", wl, dec, unique)
+    out = {"plain_decode": None, "shared_prefix_call": None}
+    if plain:
+        out["plain_decode"] = {"fetch_bytes": plain["fetch_bytes"],
+                               "write_bytes": plain["write_bytes"],
+                               "over_unique": plain["ratio_to_algorithmic"]}
+    if prefix and suffix:
+        tot = (prefix["fetch_bytes"] + prefix["write_bytes"] + suffix["fetch_bytes"] +
+               suffix["write_bytes"])
+        out["shared_prefix_call"] = {
+            "prefix_step": {"fetch_bytes": prefix["fetch_bytes"],
+                            "write_bytes": prefix["write_bytes"]},
+            "suffix_step": {"fetch_bytes": suffix["fetch_bytes"],
+                            "write_bytes": suffix["write_bytes"]},
+            "over_unique": round(tot / unique, 4)}
+    return out
 
 
 class Timer:
@@ -297,8 +332,8 @@ def main():
                 "algorithmic_bytes": nbytes}
             del case
         # ---------------- prefix-shared decode sweep ---------------------
-        if want("prefix"):
-            for B in (16, 32, 64, 128):
+        if want("prefix") or want("prefix16"):
+            for B in ((16, 32, 64, 128) if want("prefix") else (16,)):
                 case = W.prefix_shared_bf16_decode(B)
                 logical = W.decode_bytes(case, out_bytes_per_elem=2)
                 unique = (case.meta["unique_tokens"] * 8 * 128 * 2 * 2 +
@@ -321,6 +356,9 @@ def main():
                         "prefix_kernel_avg_us": round(rc["prefix_ms"] * 1e3, 2),
                         "suffix_kernel_avg_us": round(rc["part_ms"] * 1e3, 2)},
                     "unique_bytes": unique, "logical_bytes": logical}
+                if B == 16:
+                    extra["prefix-shared-bf16-decode-B16"]["dram_measured"] = \
+                        prefix_dram_measured(unique)
                 del case
         # ---------------- causal prefill, bf16 ---------------------------
         if want("prefill"):
