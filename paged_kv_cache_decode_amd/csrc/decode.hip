@@ -170,31 +170,71 @@ __device__ __forceinline__ int tiles_of(int n) { return (n + kTileKeys - 1) / kT
 __device__ __forceinline__ int cost_of(int n) { return n > 0 ? tiles_of(n) + kUnitCost : 0; }
 
 // Partial results cross workgroups (and XCDs, whose L2 caches are not
-// coherent with each other).  They are written and read with relaxed
-// device-scope atomic accesses, which the hardware performs at the coherent
+// coherent with each other).  They are written and read at the coherent
 // level (the sc1 bit) without flushing or invalidating the L2; a writer
-// waits for its stores to complete before it counts its partition.
-__device__ __forceinline__ void store_partial(float* p, float x, float y) {  // p 8-byte aligned
-  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
+// waits for its stores to complete before it counts its partition.  The
+// log-sum-exp values use relaxed device-scope atomic accesses, which the
+// compiler emits with sc1.
 __device__ __forceinline__ void store_partial(float* p, float x) {
   __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <int N>
-__device__ __forceinline__ void load_partial(const float* p, float* o) {
-  if constexpr (N == 1) {
-    o[0] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
+// The partial output rows use buffer instructions with sc1 set, so that one
+// store instruction writes whole 16-byte pieces contiguous across lanes (a
+// write-through store of 8-byte pieces at a 32-byte stride cost 3.4 times
+// the DRAM writes).  kRawBuffer is the descriptor word of a raw (untyped,
+// 32-bit element) buffer.
+constexpr int kSc1 = 16;
+constexpr int kRawBuffer = 0x00020000;
+// Layout of one head's normalised partial row (D floats) in a slot: the
+// kLPR lanes that hold the row own kE consecutive values each, and store j
+// of lane i writes that lane's values 4j .. 4j+3 at row position
+// j*4*kLPR + 4*i, so value d sits at position
+//   ((d % kE) / 4) * 4 * kLPR + 4 * (d / kE) + d % 4.
+template <int kE, int kLPR>
+__device__ __forceinline__ int partial_pos(int d) {
+  return ((d % kE) / 4) * 4 * kLPR + 4 * (d / kE) + d % 4;
+}
+template <int kE, int kLPR>
+__device__ __forceinline__ void store_partial_row(float* row, int lane, const float* v,
+                                                  float inv) {
+  // `row` is the same for the whole wave; readfirstlane puts it in scalar
+  // registers, as the descriptor needs.
+  float* const row_u = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(row)));
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(row_u, 0, kE * kLPR * 4, kRawBuffer);
 #pragma unroll
-    for (int e = 0; e < N; e += 2) {
-      const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p + e),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      o[e] = __uint_as_float((uint32_t)v);
-      o[e + 1] = __uint_as_float((uint32_t)(v >> 32));
+  for (int j = 0; j < kE / 4; ++j) {
+    const u32x4_t x = {__float_as_uint(v[4 * j] * inv), __float_as_uint(v[4 * j + 1] * inv),
+                       __float_as_uint(v[4 * j + 2] * inv), __float_as_uint(v[4 * j + 3] * inv)};
+    __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, (j * 4 * kLPR + 4 * lane) * 4, 0, kSc1);
+  }
+}
+// Values d0 .. d0+N-1 (original order, d0 a multiple of min(N, 4)) of a row
+// stored by store_partial_row; `rsrc` covers the slot's G rows.
+template <int N, int kE, int kLPR>
+__device__ __forceinline__ void load_partial_vals(__amdgpu_buffer_rsrc_t rsrc, int row_off,
+                                                  int d0, float* o) {
+  if constexpr (N == 1) {
+    o[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        rsrc, (row_off + partial_pos<kE, kLPR>(d0)) * 4, 0, kSc1));
+  } else if constexpr (N == 2) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(
+        rsrc, (row_off + partial_pos<kE, kLPR>(d0)) * 4, 0, kSc1);
+    o[0] = __uint_as_float(x[0]);
+    o[1] = __uint_as_float(x[1]);
+  } else {
+    static_assert(N % 4 == 0, "whole 16-byte pieces");
+#pragma unroll
+    for (int m = 0; m < N; m += 4) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
+          rsrc, (row_off + partial_pos<kE, kLPR>(d0 + m)) * 4, 0, kSc1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[m + k] = __uint_as_float(x[k]);
     }
   }
+}
+
+__device__ __forceinline__ float load_partial(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The shared prefix's merged state for unit (s, g), from its n_pre key
@@ -255,10 +295,15 @@ struct PrefixParts {
 template <class T, int D, int G>
 __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, int64_t slot0,
                                            int np, int lane) {
+  using Geo = DecodeGeom<T, D>;
   constexpr int kV = G * D / 64;
   static_assert(kV >= 1 && kV * 64 == G * D, "merge split");
   const int idx0 = lane * kV;
   const int h = idx0 / D, d0 = idx0 % D;
+  auto slot_rsrc = [&](int64_t slot) {
+    float* const base = a.part_o + uniform_i64(slot) * G * D;
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, G * D * 4, kRawBuffer);
+  };
   float M = -INFINITY, wsum = 0.f, acc[kV];
 #pragma unroll
   for (int e = 0; e < kV; ++e) acc[e] = 0.f;
@@ -278,8 +323,8 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, in
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int64_t slot = slot0 + p + u;
-      load_partial<1>(a.part_lse + slot * G + h, &lse[u]);
-      load_partial<kV>(a.part_o + slot * G * D + idx0, o[u]);
+      lse[u] = load_partial(a.part_lse + slot * G + h);
+      load_partial_vals<kV, Geo::kE, Geo::kLPR>(slot_rsrc(slot), h * D, d0, o[u]);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) add(lse[u], o[u]);
@@ -287,8 +332,8 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, in
   for (; p < np; ++p) {
     const int64_t slot = slot0 + p;
     float lse, o[kV];
-    load_partial<1>(a.part_lse + slot * G + h, &lse);
-    load_partial<kV>(a.part_o + slot * G * D + idx0, o);
+    lse = load_partial(a.part_lse + slot * G + h);
+    load_partial_vals<kV, Geo::kE, Geo::kLPR>(slot_rsrc(slot), h * D, d0, o);
     add(lse, o);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -666,10 +711,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
             store_out<T>(a.out, (int64_t)s * a.o_ss + (int64_t)(hq0 + h) * a.o_sh + lane * kE + e,
                          acc[h][e] * inv, a.out_f32 != 0);
         } else {
-          float* po = a.part_o + ((int64_t)(worker + u) * G + h) * D + lane * kE;
-#pragma unroll
-          for (int e = 0; e < kE; e += 2)
-            store_partial(po + e, acc[h][e] * inv, acc[h][e + 1] * inv);
+          store_partial_row<kE, Geo::kLPR>(a.part_o + ((int64_t)(worker + u) * G + h) * D, lane,
+                                           acc[h], inv);
         }
       }
     }
