@@ -749,9 +749,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
 
 template <class T, int D, int G>
 hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t stream) {
-  // The suffix step after a shared prefix (fp16 / bf16, d = 128 only) reads
-  // K as whole rows.
-  if constexpr (D == 128 && !__is_same(T, TF32)) {
+  // The suffix step after a shared prefix (fp16 / bf16, d = 128) reads K as
+  // whole rows; with groups of 8 that instance would spill registers, so
+  // those keep the operand-layout loads.
+  if constexpr (D == 128 && !__is_same(T, TF32) && G <= 4) {
     if (pl.pre_o)
       return timed_launch("decode_partitions", decode_partitions_kernel<T, D, G, true>,
                           dim3((unsigned)pl.grid[0]), dim3(pl.block_threads), stream, a);
