@@ -19,9 +19,11 @@ The same line carries:
   from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when that
   summary was taken on the current kernel source, else null.
 * ``cpu_baseline``: the fp64 CPU oracle on the same workload.
-* ``extra``: the long-context decode (4 x 100,000 keys, bf16), the
-  prefix-shared decode sweep (B = 16/32/64/128) and the causal prefill
-  (8 prompts of 512..4096 tokens, bf16; TFLOP/s against the bf16 MFMA peak).
+* ``extra``: the long-context decode (4 x 100,000 keys, bf16), the GQA and
+  long-context decodes again with pools head-major within blocks (the other
+  pool layout the library reads), the prefix-shared decode sweep
+  (B = 16/32/64/128) and the causal prefill (8 prompts of 512..4096 tokens,
+  bf16; TFLOP/s against the bf16 MFMA peak).
 """
 
 from __future__ import annotations
@@ -61,8 +63,9 @@ def parse():
                          "profiles/<KERNEL>_<WORKLOAD>_traffic.json (no GPU needed)")
     ap.add_argument("--only", default="",
                     help="comma list of workloads to run (for profiling): "
-                         "gqa,long,prefix,prefill; prefix16 runs the prefix-shared "
-                         "workload at B = 16 only")
+                         "gqa,long,gqa-hm,long-hm,prefix,prefill; prefix16 runs the "
+                         "prefix-shared workload at B = 16 only; -hm: pools head-major "
+                         "within blocks")
     return ap.parse_args()
 
 
@@ -189,11 +192,11 @@ def kernel_avg_ms(binding, name):
 
 
 def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
-                      prefix_len=None):
+                      prefix_len=None, head_major=False):
     """Time pa_decode (or pa_decode_shared_prefix with ``prefix_len``) on a
-    case, rotating over `copies` device copies of the pools.  Returns a dict
-    of timings."""
-    devs = [binding.upload_case(case) for _ in range(copies)]
+    case, rotating over `copies` device copies of the pools (token-major, or
+    head-major within blocks).  Returns a dict of timings."""
+    devs = [binding.upload_case(case, head_major) for _ in range(copies)]
     out = torch.empty(case.q.shape, dtype=out_dtype, device="cuda")
     calls = [binding.PreparedDecode(d["q"], d["k_pool"], d["v_pool"], d["block_table"],
                                     d["context_lens"], case.scale, out, prefix_len)
@@ -331,6 +334,26 @@ def main():
                 "partition_kernel_avg_us": round(r["part_ms"] * 1e3, 2),
                 "decode_workers": r["plan"]["workers"],
                 "algorithmic_bytes": nbytes}
+            del case
+        # ---- the same two workloads with head-major blocks (layout option) ----
+        for key, name, make, steps, copies, odt in (
+                ("gqa-hm", "gqa-f16-decode-head-major-blocks", W.gqa_f16_decode, a.steps, 3,
+                 torch.float16),
+                ("long-hm", "long-bf16-decode-head-major-blocks", W.long_bf16_decode,
+                 max(10, a.steps // 2), 1, torch.bfloat16)):
+            if not want(key):
+                continue
+            case = make()
+            nbytes = W.decode_bytes(case, out_bytes_per_elem=2)
+            rh = bench_decode_case(torch, binding, case, steps, 3, copies, odt,
+                                   head_major=True)
+            extra[name] = {
+                "GB/s": round(nbytes / rh["sec"] / 1e9, 1),
+                "frac_of_hbm_peak": round(nbytes / rh["sec"] / 1e9 / HBM_PEAK_GBS, 4),
+                "ms_per_step": round(rh["sec"] * 1e3, 4),
+                "partition_kernel_GB/s": round(nbytes / (rh["part_ms"] * 1e-3) / 1e9, 1),
+                "partition_kernel_avg_us": round(rh["part_ms"] * 1e3, 2),
+                "pool_layout": "[NB, Hkv, B, d] memory, viewed as [NB, B, Hkv, d]"}
             del case
         # ---------------- prefix-shared decode sweep ---------------------
         if want("prefix") or want("prefix16"):

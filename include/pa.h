@@ -31,7 +31,17 @@
  *   - Layouts (names follow the pages' domain; S sequences, H query heads,
  *     Hkv KV heads, G = H / Hkv, d head size, B block size, NB pool blocks,
  *     MB table width, T packed query rows):
- *       k_pool, v_pool   [NB, B, Hkv, d]  fully contiguous
+ *       k_pool, v_pool   [NB, B, Hkv, d]  the same layout for both, one of:
+ *                        - token-major: fully contiguous (a token's Hkv
+ *                          rows adjacent);
+ *                        - head-major within each block: element strides
+ *                          (B*Hkv*d, d, B*d, 1), i.e. a contiguous
+ *                          [NB, Hkv, B, d] buffer viewed as [NB, B, Hkv, d]
+ *                          (a KV head's B rows of a block adjacent).  On
+ *                          MI355X decode reads this layout faster: a head's
+ *                          rows then span all low address bits instead of
+ *                          one 256-byte column of every 2 KiB token row.
+ *                        Other strides return PA_ERR_STRIDE.
  *       block_table      int32 [S, MB]    last dim contiguous
  *       context_lens     int32 [S]        contiguous; n_s = keys of sequence s
  *     Logical token t of sequence s lives in physical block

@@ -353,11 +353,23 @@ def upload(a, dtype: str | None = None) -> torch.Tensor:
     return torch.from_numpy(a).cuda()
 
 
-def upload_case(case) -> dict:
-    """Device copies of a workloads.PagedCase's arrays."""
-    d = dict(q=upload(case.q, case.dtype), k_pool=upload(case.k_pool, case.dtype),
-             v_pool=upload(case.v_pool, case.dtype), block_table=upload(case.block_table),
-             context_lens=upload(case.context_lens))
+def upload_pool(a: np.ndarray, dtype: str | None = None, head_major: bool = False):
+    """A [NB, B, Hkv, d] pool on the device.  With head_major the memory is a
+    contiguous [NB, Hkv, B, d] buffer (a KV head's B rows of a block
+    adjacent) and the tensor is its [NB, B, Hkv, d] view; the library reads
+    either layout."""
+    if not head_major:
+        return upload(a, dtype)
+    return upload(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), dtype).permute(0, 2, 1, 3)
+
+
+def upload_case(case, head_major: bool = False) -> dict:
+    """Device copies of a workloads.PagedCase's arrays (pools in the
+    token-major layout, or head-major within blocks)."""
+    d = dict(q=upload(case.q, case.dtype),
+             k_pool=upload_pool(case.k_pool, case.dtype, head_major),
+             v_pool=upload_pool(case.v_pool, case.dtype, head_major),
+             block_table=upload(case.block_table), context_lens=upload(case.context_lens))
     if case.query_start_loc is not None:
         d["query_start_loc"] = upload(case.query_start_loc)
     return d

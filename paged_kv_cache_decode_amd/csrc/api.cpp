@@ -290,6 +290,7 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   pp.B = plan.B;
   pp.MB = plan.MB;
   pp.NB = plan.NB;
+  pp.pool = plan.pool;
   pp.max_query_len = plan.S;
   pp.causal = 0;
   // Workgroups of 32 query rows: the S rows are few, and smaller workgroups

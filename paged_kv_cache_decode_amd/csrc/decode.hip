@@ -102,6 +102,11 @@ struct DecodeArgs {
   int* counters;    // [Hkv * S] finished partitions per unit (g-major); zero
                     // between calls
   int S, H, Hkv, W, bs_shift;
+  // Pool layout: bytes between consecutive slots of a block, and between
+  // KV heads (token-major: Hkv*d*e and d*e; head-major blocks: d*e and
+  // B*d*e).  Blocks are Hkv*B*d*e bytes apart in both.
+  uint32_t tok_bytes;
+  int64_t head_bytes;
   float scale_log2;  // scale * log2(e)
   // Shared prefix (cascade): keys [0, key_begin) of every sequence were
   // attended by an earlier kernel in n_pre key chunks, whose normalised
@@ -457,8 +462,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   const int c = lane >> 4;    // 16-byte column group of the MFMA operands
   const int r16 = lane & 15;  // key (B operand) / head row (A operand)
   const int bmask = (1 << a.bs_shift) - 1;
-  const uint32_t tok_stride = (uint32_t)a.Hkv * Geo::kRowBytes;  // bytes between slots
-  const int64_t blk_stride = (int64_t)tok_stride << a.bs_shift;
+  const uint32_t tok_stride = a.tok_bytes;  // bytes between slots
+  const int64_t blk_stride = ((int64_t)a.Hkv * Geo::kRowBytes) << a.bs_shift;
   const int v_row = lane / Geo::kLPR;
   const uint32_t k_off = (uint32_t)r16 * tok_stride + c * 16;
   const uint32_t v_off = (uint32_t)v_row * tok_stride + (lane % Geo::kLPR) * 16;
@@ -514,8 +519,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     }
 
     const const_i32_ptr bt_row = as_const(a.bt) + (int64_t)s * a.bt_ss;
-    const uint8_t* kbase = a.k + (int64_t)g * Geo::kRowBytes;
-    const uint8_t* vbase = a.v + (int64_t)g * Geo::kRowBytes;
+    const uint8_t* kbase = a.k + (int64_t)g * a.head_bytes;
+    const uint8_t* vbase = a.v + (int64_t)g * a.head_bytes;
 
     float m[G], l_lane[G], acc[G][kE];
 #pragma unroll
@@ -862,6 +867,8 @@ hipError_t launch_decode(const DecodePlan& pl, void* workspace, hipStream_t stre
   a.Hkv = pl.Hkv;
   a.W = pl.workers;
   a.bs_shift = __builtin_ctz(pl.B);
+  a.tok_bytes = (uint32_t)(pl.pool.tok * e);
+  a.head_bytes = pl.pool.head * e;
   a.scale_log2 = pl.scale * 1.4426950408889634f;
   a.key_begin = pl.key_begin;
   a.n_pre = pl.n_pre;

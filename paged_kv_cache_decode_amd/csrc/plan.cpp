@@ -80,8 +80,10 @@ bool supported_block(int64_t B) { return B == 16 || B == 32 || B == 64 || B == 1
 
 bool supported_group(int64_t G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 
-// Pools: [NB, B, Hkv, d], contiguous, same shape and dtype for K and V.
-int check_pools(const pa_tensor* k, const pa_tensor* v, std::string* err) {
+// Pools: [NB, B, Hkv, d], same shape, dtype and layout (PoolLayout) for K
+// and V.
+int check_pools(const pa_tensor* k, const pa_tensor* v, std::string* err,
+                PoolLayout* layout = nullptr) {
   int st;
   if ((st = check_basic(k, "k_pool", 4, err, false))) return st;
   if ((st = check_basic(v, "v_pool", 4, err, false))) return st;
@@ -91,8 +93,28 @@ int check_pools(const pa_tensor* k, const pa_tensor* v, std::string* err) {
   for (int i = 0; i < 4; ++i)
     if (k->shape[i] != v->shape[i])
       return fail(err, PA_ERR_SHAPE, "k_pool and v_pool shapes differ in dim %d", i);
-  if (!contiguous(k) || !contiguous(v))
-    return fail(err, PA_ERR_STRIDE, "k_pool and v_pool must be fully contiguous");
+  const int64_t B = k->shape[1], Hkv = k->shape[2], D = k->shape[3];
+  auto layout_of = [&](const pa_tensor* t, PoolLayout* l) {
+    if (contiguous(t)) {
+      l->tok = Hkv * D;
+      l->head = D;
+      return true;
+    }
+    if (t->stride[3] == 1 && t->stride[2] == B * D && t->stride[1] == D &&
+        (t->stride[0] == B * Hkv * D || t->shape[0] == 1)) {
+      l->tok = D;
+      l->head = B * D;
+      return true;
+    }
+    return false;
+  };
+  PoolLayout lk, lv;
+  if (!layout_of(k, &lk) || !layout_of(v, &lv))
+    return fail(err, PA_ERR_STRIDE, "pools must be contiguous [NB, B, Hkv, d], or head-major "
+                "within blocks (strides B*Hkv*d, d, B*d, 1)");
+  if (lk.tok != lv.tok || lk.head != lv.head)
+    return fail(err, PA_ERR_STRIDE, "k_pool and v_pool must have the same layout");
+  if (layout) *layout = lk;
   if (!aligned16(k->data) || !aligned16(v->data))
     return fail(err, PA_ERR_STRIDE, "pool base pointers must be 16-byte aligned");
   if (k->data == v->data)
@@ -155,7 +177,8 @@ int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_
                 const pa_tensor* out, int workers, DecodePlan* plan, std::string* err) {
   int st;
   if ((st = check_rows(q, "q", err))) return st;
-  if ((st = check_pools(k_pool, v_pool, err))) return st;
+  PoolLayout layout;
+  if ((st = check_pools(k_pool, v_pool, err, &layout))) return st;
   if ((st = check_i32(block_table, "block_table", 2, err))) return st;
   if ((st = check_i32(context_lens, "context_lens", 1, err))) return st;
   if ((st = check_rows(out, "out", err))) return st;
@@ -230,6 +253,7 @@ int plan_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_
   p.ws_bytes = p.counter_bytes + p.slots * G * D * 4 + p.slots * G * 4;
   p.q = q->data; p.q_ss = q->stride[0]; p.q_sh = q->stride[1];
   p.k = k_pool->data; p.v = v_pool->data;
+  p.pool = layout;
   p.bt = static_cast<const int32_t*>(block_table->data); p.bt_ss = block_table->stride[0];
   p.cl = static_cast<const int32_t*>(context_lens->data);
   p.out = out->data; p.o_ss = out->stride[0]; p.o_sh = out->stride[1];
@@ -244,7 +268,8 @@ int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v
                  int32_t causal, const pa_tensor* out, PrefillPlan* plan, std::string* err) {
   int st;
   if ((st = check_rows(q, "q", err))) return st;
-  if ((st = check_pools(k_pool, v_pool, err))) return st;
+  PoolLayout layout;
+  if ((st = check_pools(k_pool, v_pool, err, &layout))) return st;
   if ((st = check_i32(block_table, "block_table", 2, err))) return st;
   if ((st = check_i32(context_lens, "context_lens", 1, err))) return st;
   if ((st = check_i32(query_start_loc, "query_start_loc", 1, err))) return st;
@@ -314,6 +339,7 @@ int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v
   p.block_threads = 64 * p.row_waves * (int)(G / kv_div);  // 32 positions of one head per wave
   p.q = q->data; p.q_st = q->stride[0]; p.q_sh = q->stride[1];
   p.k = k_pool->data; p.v = v_pool->data;
+  p.pool = layout;
   p.bt = static_cast<const int32_t*>(block_table->data); p.bt_ss = block_table->stride[0];
   p.cl = static_cast<const int32_t*>(context_lens->data);
   p.qsl = static_cast<const int32_t*>(query_start_loc->data);
@@ -330,7 +356,8 @@ int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
   if ((st = check_rows(k_new, "k_new", err))) return st;
   if ((st = check_rows(v_new, "v_new", err))) return st;
   if ((st = check_i32(slot_mapping, "slot_mapping", 1, err))) return st;
-  if ((st = check_pools(k_pool, v_pool, err))) return st;
+  PoolLayout layout;
+  if ((st = check_pools(k_pool, v_pool, err, &layout))) return st;
   if (k_new->dtype != k_pool->dtype || v_new->dtype != k_pool->dtype)
     return fail(err, PA_ERR_DTYPE, "new rows and pools must share a dtype");
   if (!is_float(k_pool->dtype)) return fail(err, PA_ERR_DTYPE, "pools must be f32/f16/bf16");
@@ -361,6 +388,7 @@ int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
   p.vn_s = v_new->stride[0]; p.vn_h = v_new->stride[1];
   p.slots = static_cast<const int32_t*>(slot_mapping->data);
   p.kp = k_pool->data; p.vp = v_pool->data;
+  p.pool = layout;
   *plan = p;
   return PA_OK;
 }

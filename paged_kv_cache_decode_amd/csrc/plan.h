@@ -18,6 +18,18 @@ namespace pa {
 // slices, one per worker.  A worker's piece of one unit is a partition;
 // the last worker to finish a split unit joins its partitions.
 constexpr int kDecodeWaves = 4;
+
+// Element strides of a pool's token and KV-head dimensions.  Pools are
+// logically [NB, B, Hkv, d] in one of two layouts (the same for K and V):
+//   token-major: fully contiguous, a token's Hkv rows adjacent (tok = Hkv*d,
+//     head = d);
+//   head-major within each block: strides (B*Hkv*d, d, B*d, 1), i.e. a
+//     contiguous [NB, Hkv, B, d] buffer, a head's B rows adjacent (tok = d,
+//     head = B*d).
+struct PoolLayout {
+  int64_t tok = 0;
+  int64_t head = 0;
+};
 constexpr int kTileKeys = 16;
 constexpr int kMaxWorkers = 1 << 20;
 
@@ -26,6 +38,7 @@ struct DecodePlan {
   int out_dtype = 0;  // PA_F32 or dtype
   int S = 0, H = 0, Hkv = 0, G = 0, D = 0, B = 0, MB = 0;
   int64_t NB = 0;
+  PoolLayout pool;
   int workers = 0;       // wavefronts launched
   int64_t slots = 0;     // partial-result slots: workers + S * Hkv
   int64_t grid[3] = {0, 0, 0};
@@ -61,6 +74,7 @@ struct PrefillPlan {
   int dtype = 0, out_dtype = 0;
   int S = 0, T = 0, H = 0, Hkv = 0, G = 0, D = 0, B = 0, MB = 0;
   int64_t NB = 0;
+  PoolLayout pool;
   int max_query_len = 0;
   int causal = 0;
   int row_waves = kPrefillRowWaves;  // waves per head: 32 * row_waves query rows per workgroup
@@ -96,6 +110,7 @@ struct WriteKvPlan {
   int dtype = 0;
   int64_t N = 0, NB = 0;
   int B = 0, Hkv = 0, D = 0;
+  PoolLayout pool;
   const void* kn = nullptr;
   const void* vn = nullptr;
   int64_t kn_s = 0, kn_h = 0, vn_s = 0, vn_h = 0;

@@ -71,6 +71,10 @@ struct PrefillArgs {
   int64_t o_st, o_sh;  // elements
   int out_f32;
   int S, Hkv, MB, q_tiles, bs_shift, causal;
+  // Pool layout (bytes): between consecutive slots of a block, and between
+  // KV heads; blocks are Hkv*B*d*2 bytes apart.
+  int tok_bytes;
+  int64_t head_bytes;
   uint32_t q_sign;     // XORed into Q's 16-bit lanes (0x80008000 when scale < 0)
   // Head groups of more than 4 heads run as kv_div workgroups of 4 heads per
   // KV head (each reads that KV head's K/V): workgroup group g covers query
@@ -212,11 +216,11 @@ __global__ __launch_bounds__(64 * RW * G) void prefill_kernel(PrefillArgs a) {
   }
 
   const const_i32_ptr bt_row = as_const(a.bt) + (int64_t)s * a.bt_ss;
-  const int tok_stride = a.Hkv * kD * 2;  // bytes between consecutive slots
+  const int tok_stride = a.tok_bytes;  // bytes between consecutive slots
   const int bmask = (1 << a.bs_shift) - 1;
-  const int64_t block_bytes = (int64_t)tok_stride << a.bs_shift;
-  const uint8_t* kbase = a.k + (int64_t)(g / a.kv_div) * kD * 2;
-  const uint8_t* vbase = a.v + (int64_t)(g / a.kv_div) * kD * 2;
+  const int64_t block_bytes = (int64_t)(a.Hkv * kD * 2) << a.bs_shift;
+  const uint8_t* kbase = a.k + (int64_t)(g / a.kv_div) * a.head_bytes;
+  const uint8_t* vbase = a.v + (int64_t)(g / a.kv_div) * a.head_bytes;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index (uniform)
   // Gather addressing.  Every load instruction of a wave covers 4 (K) or 8
   // (V) consecutive keys starting at a multiple of 4 (8), so all its lanes
@@ -529,6 +533,8 @@ hipError_t launch_prefill(const PrefillPlan& pl, hipStream_t stream) {
   a.MB = pl.MB;
   a.q_tiles = pl.q_tiles;
   a.bs_shift = __builtin_ctz(pl.B);
+  a.tok_bytes = (int)(pl.pool.tok * 2);
+  a.head_bytes = pl.pool.head * 2;
   a.causal = pl.causal;
   // A negative scale is applied by negating Q (exact in 16-bit formats) so
   // that the softmax always works with c >= 0.

@@ -21,6 +21,8 @@ struct WriteKvArgs {
   uint8_t* vp;
   int64_t N;
   int Hkv, row_bytes, chunks;  // chunks = row_bytes / 16
+  int B;
+  int64_t blk_bytes, tok_bytes, head_bytes;  // pool layout
 };
 
 __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
@@ -32,9 +34,9 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteKvArgs a) {
   const int h = rem / a.chunks, ch = rem % a.chunks;
   const int32_t slot = a.slots[i];
   if (slot < 0) return;
-  // Slot x is block x / B, position x % B; with the pool contiguous that is
-  // simply row x of the [NB * B, Hkv, d] view.
-  const int64_t dst = ((int64_t)slot * a.Hkv + h) * a.row_bytes + ch * 16;
+  // Slot x is block x / B, position x % B.
+  const int64_t dst = (int64_t)(slot / a.B) * a.blk_bytes + (int64_t)(slot % a.B) * a.tok_bytes +
+                      h * a.head_bytes + ch * 16;
   *reinterpret_cast<u32x4_t*>(a.kp + dst) = load16(a.kn + i * a.kn_s + h * a.kn_h + ch * 16);
   *reinterpret_cast<u32x4_t*>(a.vp + dst) = load16(a.vn + i * a.vn_s + h * a.vn_h + ch * 16);
 }
@@ -57,6 +59,10 @@ hipError_t launch_write_kv(const WriteKvPlan& pl, hipStream_t stream) {
   a.Hkv = pl.Hkv;
   a.row_bytes = pl.D * e;
   a.chunks = a.row_bytes / 16;
+  a.B = pl.B;
+  a.blk_bytes = (int64_t)pl.B * pl.Hkv * pl.D * e;
+  a.tok_bytes = pl.pool.tok * e;
+  a.head_bytes = pl.pool.head * e;
   const int64_t total = pl.N * pl.Hkv * a.chunks;
   if (total == 0) return hipSuccess;
   return timed_launch("write_kv", write_kv_kernel, dim3((unsigned)((total + 255) / 256)),

@@ -23,9 +23,17 @@ def to_dev(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
     return t.cuda()
 
 
-def case_to_dev(c):
-    return dict(q=to_dev(c.q, c.dtype), k_pool=to_dev(c.k_pool, c.dtype),
-                v_pool=to_dev(c.v_pool, c.dtype), block_table=to_dev(c.block_table),
+def pool_to_dev(a: np.ndarray, dtype: str, head_major: bool = False) -> torch.Tensor:
+    """A [NB, B, Hkv, d] pool on the GPU; with head_major its memory is a
+    contiguous [NB, Hkv, B, d] buffer viewed as [NB, B, Hkv, d]."""
+    if not head_major:
+        return to_dev(a, dtype)
+    return to_dev(np.ascontiguousarray(a.transpose(0, 2, 1, 3)), dtype).permute(0, 2, 1, 3)
+
+
+def case_to_dev(c, head_major: bool = False):
+    return dict(q=to_dev(c.q, c.dtype), k_pool=pool_to_dev(c.k_pool, c.dtype, head_major),
+                v_pool=pool_to_dev(c.v_pool, c.dtype, head_major), block_table=to_dev(c.block_table),
                 context_lens=to_dev(c.context_lens),
                 query_start_loc=None if c.query_start_loc is None else to_dev(c.query_start_loc))
 

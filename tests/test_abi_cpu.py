@@ -201,3 +201,28 @@ def test_write_kv_rejects():
     sm = T([10], B.PA_I32, 3 * GAP)
     kp2 = T([4, 16, 8, 128], B.PA_F16, 4 * GAP)
     assert B.lib().pa_write_kv(r(kn), r(vn), r(sm), r(kp2), r(vp), None) == -2
+
+
+def head_major(t, NB=100, Bs=16, Hkv=8, d=128):
+    """The same logical [NB, B, Hkv, d] pool with head-major blocks: strides
+    of a contiguous [NB, Hkv, B, d] buffer."""
+    for i, s in enumerate([Bs * Hkv * d, d, Bs * d, 1]):
+        t.stride[i] = s
+    return t
+
+
+def test_pool_layouts():
+    """Both pool layouts plan; other strides, or K and V in different
+    layouts, are rejected before any GPU work."""
+    a = decode_args()
+    head_major(a["k"]), head_major(a["v"])
+    assert plan(a)[0] == 0
+    b = decode_args()
+    head_major(b["k"])  # K head-major, V token-major
+    assert call_decode(b) == -4
+    assert "same layout" in B.lib().pa_last_error().decode()
+    c = decode_args()
+    for t in (c["k"], c["v"]):
+        head_major(t)
+        t.stride[1], t.stride[2] = 2 * 128, 16 * 128  # rows of a head not adjacent
+    assert call_decode(c) == -4
