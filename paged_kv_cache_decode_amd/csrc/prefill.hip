@@ -144,9 +144,13 @@ __device__ __forceinline__ float swap_halves(float x) {
 // adjacent); it spreads the transposing writes over the LDS banks.
 __device__ __forceinline__ int vt_col(int d, int kp) { return kp ^ ((d >> 5) << 1); }
 
-// RW waves per head: a workgroup covers 32 * RW query positions.
+// RW waves per head: a workgroup covers 32 * RW query positions.  The
+// 32-row instances (the shared-prefix step) ask for at most half the
+// register file, so that two of their workgroups can share a CU (measured:
+// prefix step 28 -> 25.5 us on the shared-prefix workload).
 template <class T, int G, int RW>
-__global__ __launch_bounds__(64 * RW * G) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * RW * G)
+__attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(PrefillArgs a) {
   constexpr int kNT = 64 * RW * G;  // threads
   constexpr int kRows = 32 * RW;    // query positions per workgroup
   constexpr int kKPer = kKChunks / kNT;
