@@ -4,8 +4,8 @@ compute call, each checked against the CPU oracle.
 The fixed tests pin chosen edge cases; these draw the shape (dtype, head
 size, group size, KV heads, block size, batch), the length mix (empty,
 single-key, short, long contexts), the scale (including negative and
-large) and the decode worker count, so that combinations nobody listed are
-exercised too.  Every draw is seeded: a failure names its seed."""
+large), the decode worker count and the pool layout, so that combinations
+nobody listed are exercised too.  Every draw is seeded: a failure names its seed."""
 
 import numpy as np
 import pytest
@@ -51,11 +51,12 @@ def test_decode_random_configs(pa, monkeypatch, seed):
     else:
         monkeypatch.delenv("PA_DECODE_WORKERS", raising=False)
     lens = draw_lens(rng, S)
+    hm = bool(rng.integers(0, 2))  # pool layout: head-major within blocks
     what = (f"seed={seed} {dtype} d={d} G={G} Hkv={Hkv} B={B} S={S} scale={scale} "
-            f"workers={workers or 'default'}")
+            f"workers={workers or 'default'} head_major={hm}")
     print(what, flush=True)
     c = W.make_decode_case(6000 + seed, S, G * Hkv, Hkv, d, B, dtype, lens=lens, scale=scale)
-    dev = case_to_dev(c)
+    dev = case_to_dev(c, head_major=hm)
     ref, _ = oracle.decode(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale,
                            c.dtype)
     got = pa.decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_table"],
@@ -82,12 +83,13 @@ def test_prefill_random_configs(pa, seed):
     lens = [int(x) for x in rng.integers(1, 700, size=S)]
     # Whole prompts or the last L_q positions of a longer context.
     qlens = [n if rng.random() < 0.5 else int(rng.integers(1, n + 1)) for n in lens]
+    hm = bool(rng.integers(0, 2))
     what = (f"seed={seed} {dtype} G={G} Hkv={Hkv} B={B} S={S} causal={causal} "
-            f"scale={scale} lens={lens} qlens={qlens}")
+            f"scale={scale} lens={lens} qlens={qlens} head_major={hm}")
     print(what, flush=True)
     c = W.make_prefill_case(8000 + seed, S, G * Hkv, Hkv, 128, B, dtype, lens=lens,
                             query_lens=qlens, causal=causal, scale=scale)
-    dev = case_to_dev(c)
+    dev = case_to_dev(c, head_major=hm)
     got = out_to_f64(pa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_table"],
                                 dev["context_lens"], dev["query_start_loc"], c.max_query_len,
                                 c.scale, causal=c.causal, out_dtype=torch.float32))
@@ -111,13 +113,14 @@ def test_shared_prefix_random_configs(pa, seed):
     prefix_len = B * int(rng.integers(1, 40))
     hi = int(rng.choice([0, 50, 700]))
     dtype = str(rng.choice(["f16", "bf16"]))
+    hm = bool(rng.integers(0, 2))
     what = (f"seed={seed} {dtype} G={G} Hkv={Hkv} B={B} S={S} prefix={prefix_len} "
-            f"suffix<={hi}")
+            f"suffix<={hi} head_major={hm}")
     print(what, flush=True)
     c = W.make_prefix_shared_case(9100 + seed, B, num_seqs=S, prefix_len=prefix_len,
                                   suffix_range=(0, hi), num_heads=G * Hkv,
                                   num_kv_heads=Hkv, dtype=dtype)
-    dev = case_to_dev(c)
+    dev = case_to_dev(c, head_major=hm)
     got = out_to_f64(pa.decode_shared_prefix(dev["q"], dev["k_pool"], dev["v_pool"],
                                              dev["block_table"], dev["context_lens"],
                                              prefix_len, c.scale, out_dtype=torch.float32))
