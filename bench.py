@@ -22,8 +22,9 @@ The same line carries:
 * ``extra``: the long-context decode (4 x 100,000 keys, bf16), the GQA and
   long-context decodes again with pools head-major within blocks (the other
   pool layout the library reads), the prefix-shared decode sweep
-  (B = 16/32/64/128) and the causal prefill (8 prompts of 512..4096 tokens,
-  bf16; TFLOP/s against the bf16 MFMA peak).
+  (B = 16/32/64/128), the causal prefill (8 prompts of 512..4096 tokens,
+  bf16; TFLOP/s against the bf16 MFMA peak) and, as context for the HBM
+  fractions, the rate of a plain 1 GiB device copy.
 """
 
 from __future__ import annotations
@@ -222,6 +223,24 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
     torch.cuda.empty_cache()
     return dict(sec=sec, part_ms=part_ms, part_launches=part_n, plan=plan,
                 prefix_ms=pre_ms if pre_n else 0.0)
+
+
+def copy_bandwidth(torch, reps=10):
+    """Attainable HBM rate for context: a 1 GiB device-to-device copy (1 GiB
+    read + 1 GiB written per call), wall clock over `reps` calls."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * (1 << 30) / sec / 1e9
 
 
 def cpu_oracle_decode(case, budget_s=10.0, max_passes=8):
@@ -447,6 +466,12 @@ def main():
                               f"{wall:.1f} s"}
             extra["causal-bf16-prefill"] = entry
             del d, call
+    if not a.headline_only and (not only or "copy" in only):
+        gbs = copy_bandwidth(torch)
+        extra["device_copy"] = {
+            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": "attainable-rate context: torch copy of 1 GiB (1 GiB read + 1 GiB "
+                    "written per call)"}
     if extra:
         result["extra"] = extra
     if not result:
