@@ -144,6 +144,43 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_po
               const pa_tensor* out, void* stream);
 
 /*
+ * pa_decode_lse -- pa_decode that also returns each (sequence, query head)'s
+ * log-sum-exp of the scaled scores, lse = ln sum_t e^(scale * q . k_t)
+ * (-inf for n_s = 0).  With the normalised output it is the state the
+ * online softmax carries ("FlashAttention and PagedAttention: two fixes for
+ * two different bottlenecks", "FlashAttention - How it works": running
+ * maximum and sum), so the attention over a context split into disjoint key
+ * sets -- e.g. the contiguous block ranges that several GPUs each hold of a
+ * very long context -- is recovered exactly by pa_merge_states.
+ *   lse   f32 [S, H], last dim contiguous, 4-byte aligned, not aliasing
+ *         q, the pools or out.  NULL returns PA_ERR_NULL.
+ * Everything else as pa_decode.
+ */
+int pa_decode_lse(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                  const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+                  const pa_tensor* out, const pa_tensor* lse, void* stream);
+
+/*
+ * pa_merge_states -- joins P partial attention states of every
+ * (sequence, head), each over a disjoint set of keys (pa_decode_lse's out
+ * and lse on each set):
+ *   M = max_p lse_p,  w_p = e^(lse_p - M),
+ *   out = sum_p w_p out_p / sum_p w_p,  lse = M + ln sum_p w_p,
+ * the online softmax's rescaling applied to whole parts ("FlashAttention -
+ * How it works").  Parts with lse_p = -inf hold no key and contribute
+ * nothing; if every part is empty, out = 0 and lse = -inf.
+ *   part_out   f32 [P, S, H, d], d in {64, 128}, last dim contiguous, P >= 1
+ *   part_lse   f32 [P, S, H]
+ *   out        [S, H, d], f32, f16 or bf16 (rounded to nearest even), last
+ *              dim contiguous, rows 16-byte aligned
+ *   lse        f32 [S, H] merged log-sum-exp, or NULL
+ * Strides of the other dimensions are free.  out and lse must not alias the
+ * parts.  Stream-ordered; no workspace.
+ */
+int pa_merge_states(const pa_tensor* part_out, const pa_tensor* part_lse, const pa_tensor* out,
+                    const pa_tensor* lse, void* stream);
+
+/*
  * pa_prefill -- packed query rows of several sequences attend to their paged
  * KV caches, optionally with a causal mask.
  *

@@ -66,6 +66,8 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(PaTensor)
     L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, ctypes.c_void_p]
+    L.pa_decode_lse.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_void_p]
+    L.pa_merge_states.argtypes = [P, P, P, P, ctypes.c_void_p]
     L.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.c_float, P,
                                           ctypes.c_void_p]
     L.pa_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
@@ -87,7 +89,8 @@ def lib():
     L.pa_bm_take_copies.argtypes = [V, I32P, I32P, ctypes.c_int32]
     L.pa_bm_free.argtypes = [V, ctypes.c_int64]
     L.pa_bm_block_table.argtypes = [V, I64P, ctypes.c_int32, ctypes.c_int32, I32P, I32P]
-    for f in ("pa_decode", "pa_decode_shared_prefix", "pa_prefill", "pa_write_kv",
+    for f in ("pa_decode", "pa_decode_lse", "pa_merge_states", "pa_decode_shared_prefix",
+              "pa_prefill", "pa_write_kv",
               "pa_copy_blocks", "pa_decode_plan",
               "pa_workspace_release", "pa_profiler_enable", "pa_profiler_read", "pa_bm_num_free",
               "pa_bm_refcount", "pa_bm_add", "pa_bm_fork", "pa_bm_append", "pa_bm_take_copies",
@@ -150,6 +153,39 @@ def decode(q, k_pool, v_pool, block_table, context_lens, scale, out=None, out_dt
     _check(L.pa_decode(*[ctypes.byref(a) for a in args], ctypes.c_float(scale),
                        ctypes.byref(o), _stream(stream)))
     return out
+
+
+def decode_lse(q, k_pool, v_pool, block_table, context_lens, scale, out=None, lse=None,
+               out_dtype=None, stream=None):
+    """Paged decode that also returns each (sequence, head)'s natural-log
+    log-sum-exp: ``(out [S, H, d], lse [S, H] f32)`` (see ``pa_decode_lse``)."""
+    L = lib()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens)]
+    o, ls = describe(out), describe(lse)
+    _check(L.pa_decode_lse(*[ctypes.byref(a) for a in args], ctypes.c_float(scale),
+                           ctypes.byref(o), ctypes.byref(ls), _stream(stream)))
+    return out, lse
+
+
+def merge_states(part_out, part_lse, out=None, lse=None, out_dtype=torch.float32,
+                 want_lse=True, stream=None):
+    """Join partial attention states ``part_out [P, S, H, d]`` (f32) with
+    their log-sum-exps ``part_lse [P, S, H]``; returns ``(out, lse)`` (lse
+    None unless wanted) -- see ``pa_merge_states``."""
+    L = lib()
+    if out is None:
+        out = torch.empty(part_out.shape[1:], dtype=out_dtype, device=part_out.device)
+    if lse is None and want_lse:
+        lse = torch.empty(part_out.shape[1:3], dtype=torch.float32, device=part_out.device)
+    a, b, o = describe(part_out), describe(part_lse), describe(out)
+    ls = describe(lse) if lse is not None else None
+    _check(L.pa_merge_states(ctypes.byref(a), ctypes.byref(b), ctypes.byref(o),
+                             ctypes.byref(ls) if ls is not None else None, _stream(stream)))
+    return out, lse
 
 
 def decode_shared_prefix(q, k_pool, v_pool, block_table, context_lens, prefix_len, scale,

@@ -227,19 +227,25 @@ int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor*
   return PA_OK;
 }
 
-int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
-              const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
-              const pa_tensor* out, void* stream_ptr) {
+namespace {
+
+int decode_impl(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+                const pa_tensor* out, const pa_tensor* lse, void* stream_ptr) {
   g_last_error.clear();
   pa::DecodePlan plan;
   // Validate first (no device query for invalid arguments), then size.
   int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out, 1, &plan,
                            &g_last_error);
   if (st) return st;
+  if (lse && (st = pa::plan_decode_lse(lse, q, k_pool, v_pool, out, &plan, &g_last_error)))
+    return st;
   if (plan.S == 0) return PA_OK;
   st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out,
                        decode_workers(q, k_pool), &plan, &g_last_error);
   if (st) return st;
+  if (lse && (st = pa::plan_decode_lse(lse, q, k_pool, v_pool, out, &plan, &g_last_error)))
+    return st;
   if (log_enabled())
     fprintf(stderr,
             "[pa] decode dtype=%d out=%d S=%d H=%d Hkv=%d d=%d B=%d MB=%d workers=%d "
@@ -252,6 +258,38 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_po
   if (st) return st;
   const hipError_t e = pa::launch_decode(plan, ws, stream);
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // namespace
+
+int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+              const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+              const pa_tensor* out, void* stream_ptr) {
+  return decode_impl(q, k_pool, v_pool, block_table, context_lens, scale, out, nullptr,
+                     stream_ptr);
+}
+
+int pa_decode_lse(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                  const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+                  const pa_tensor* out, const pa_tensor* lse, void* stream_ptr) {
+  if (!lse) {
+    g_last_error.clear();
+    return set_error(PA_ERR_NULL, "lse is NULL");
+  }
+  return decode_impl(q, k_pool, v_pool, block_table, context_lens, scale, out, lse,
+                     stream_ptr);
+}
+
+int pa_merge_states(const pa_tensor* part_out, const pa_tensor* part_lse, const pa_tensor* out,
+                    const pa_tensor* lse, void* stream_ptr) {
+  g_last_error.clear();
+  if (!part_out || !part_lse || !out) return set_error(PA_ERR_NULL, "a tensor is NULL");
+  pa::MergePlan plan;
+  const int st = pa::plan_merge(part_out, part_lse, out, lse, &plan, &g_last_error);
+  if (st) return st;
+  const hipError_t e = pa::launch_merge(plan, static_cast<hipStream_t>(stream_ptr));
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "merge launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

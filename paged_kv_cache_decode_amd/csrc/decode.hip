@@ -119,7 +119,13 @@ struct DecodeArgs {
   int n_pre;
   const float* pre_o;
   const float* pre_lse;
+  // Optional natural-log log-sum-exp per (s, query head): lse_out[s *
+  // lse_ss + h], or nullptr.
+  float* lse_out;
+  int64_t lse_ss;
 };
+
+constexpr float kLn2 = 0.6931471805599453f;
 
 // S = Q K^T on matrix cores for one 16-key tile.  Returns, per lane, the
 // scores of key r16 for heads h < G in elements 0..G-1.
@@ -342,6 +348,9 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, in
     add(lse, o);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if (a.lse_out && d0 == 0)
+    a.lse_out[(int64_t)s * a.lse_ss + g * G + h] = wsum > 0.f ? (M + __log2f(wsum)) * kLn2
+                                                              : -INFINITY;
   const int64_t ob = (int64_t)s * a.o_ss + (int64_t)(g * G + h) * a.o_sh + d0;
 #pragma unroll
   for (int e = 0; e < kV; ++e) store_out<T>(a.out, ob + e, acc[e] * inv, a.out_f32 != 0);
@@ -374,6 +383,7 @@ __device__ __forceinline__ void zero_empty_units(const DecodeArgs& a, int worker
         for (int i = lane; i < G * D; i += 64)
           store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
                        0.f, a.out_f32 != 0);
+        if (a.lse_out && lane < G) a.lse_out[(int64_t)su * a.lse_ss + gu * G + lane] = -INFINITY;
       }
     }
   }
@@ -721,6 +731,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
         }
       }
     }
+    if (whole && a.lse_out && lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        a.lse_out[(int64_t)s * a.lse_ss + hq0 + h] = (m[h] + __log2f(l_lane[h])) * kLn2;
+    }
     if (!whole) {
       if (lane == 0) {
 #pragma unroll
@@ -874,12 +889,111 @@ hipError_t launch_decode(const DecodePlan& pl, void* workspace, hipStream_t stre
   a.n_pre = pl.n_pre;
   a.pre_o = pl.pre_o;
   a.pre_lse = pl.pre_lse;
+  a.lse_out = pl.lse;
+  a.lse_ss = pl.lse_ss;
   switch (pl.dtype) {
     case PA_F32: return dispatch_shape<TF32>(pl, a, stream);
     case PA_F16: return dispatch_shape<TF16>(pl, a, stream);
     case PA_BF16: return dispatch_shape<TBF16>(pl, a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+
+namespace {
+
+// Joins P partial attention states of each (s, h): the part p attended a
+// disjoint key set and gives its normalised output o_p and natural-log
+// log-sum-exp lse_p.  With M = max_p lse_p and w_p = e^(lse_p - M):
+//   out = sum_p w_p o_p / sum_p w_p,   lse = M + ln sum_p w_p
+// -- the rescaling of the online softmax's running maximum and sum
+// ("FlashAttention and PagedAttention: two fixes for two different
+// bottlenecks", "FlashAttention - How it works"), applied to whole parts.
+// Parts with lse = -inf attended no key; if all are, out = 0 and lse = -inf.
+// One wavefront per (s, h); lane l holds values l*kV .. l*kV+kV-1.
+struct MergeArgs {
+  const float* po;
+  int64_t po_p, po_s, po_h;
+  const float* pl;
+  int64_t pl_p, pl_s, pl_h;
+  void* out;
+  int64_t o_s, o_h;
+  int out_dtype;
+  float* lse;
+  int64_t l_s, l_h;
+  int P, S, H;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_states_kernel(MergeArgs a) {
+  constexpr int kV = D / 64;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (unit >= (int64_t)a.S * a.H) return;
+  const int s = (int)(unit / a.H), h = (int)(unit % a.H);
+  const float* lp = a.pl + (int64_t)s * a.pl_s + (int64_t)h * a.pl_h;
+  float M = -INFINITY;
+  for (int p = 0; p < a.P; ++p) M = fmaxf(M, lp[(int64_t)p * a.pl_p]);
+  float acc[kV], wsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < kV; ++e) acc[e] = 0.f;
+  if (M != -INFINITY) {
+    const float* op = a.po + (int64_t)s * a.po_s + (int64_t)h * a.po_h + lane * kV;
+    for (int p = 0; p < a.P; ++p) {
+      const float l = lp[(int64_t)p * a.pl_p];
+      if (l == -INFINITY) continue;
+      const float w = fast_exp2((l - M) * 1.4426950408889634f);
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < kV; ++e) acc[e] = fmaf(w, op[(int64_t)p * a.po_p + e], acc[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t ob = (int64_t)s * a.o_s + (int64_t)h * a.o_h + lane * kV;
+#pragma unroll
+  for (int e = 0; e < kV; ++e) {
+    const float v = acc[e] * inv;
+    if (a.out_dtype == PA_F32)
+      static_cast<float*>(a.out)[ob + e] = v;
+    else if (a.out_dtype == PA_F16)
+      static_cast<uint16_t*>(a.out)[ob + e] = to_f16_bits(v);
+    else
+      static_cast<uint16_t*>(a.out)[ob + e] = to_bf16_bits(v);
+  }
+  if (a.lse && lane == 0)
+    a.lse[(int64_t)s * a.l_s + (int64_t)h * a.l_h] =
+        wsum > 0.f ? M + __log2f(wsum) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergePlan& pl, hipStream_t stream) {
+  MergeArgs a;
+  a.po = pl.part_out;
+  a.po_p = pl.po_p;
+  a.po_s = pl.po_s;
+  a.po_h = pl.po_h;
+  a.pl = pl.part_lse;
+  a.pl_p = pl.pl_p;
+  a.pl_s = pl.pl_s;
+  a.pl_h = pl.pl_h;
+  a.out = pl.out;
+  a.o_s = pl.o_s;
+  a.o_h = pl.o_h;
+  a.out_dtype = pl.out_dtype;
+  a.lse = pl.lse;
+  a.l_s = pl.l_s;
+  a.l_h = pl.l_h;
+  a.P = pl.P;
+  a.S = pl.S;
+  a.H = pl.H;
+  const int64_t units = (int64_t)pl.S * pl.H;
+  if (units == 0) return hipSuccess;
+  const dim3 grid((unsigned)((units + 3) / 4));
+  return pl.D == 64 ? timed_launch("merge_states", merge_states_kernel<64>, grid, dim3(256),
+                                   stream, a)
+                    : timed_launch("merge_states", merge_states_kernel<128>, grid, dim3(256),
+                                   stream, a);
 }
 
 }  // namespace pa

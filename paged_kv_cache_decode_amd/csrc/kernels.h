@@ -19,6 +19,9 @@ int decode_worker_count(int dtype, int D, int G);
 
 hipError_t launch_prefill(const PrefillPlan& plan, hipStream_t stream);
 
+// Joins partial attention states (pa_merge_states).
+hipError_t launch_merge(const MergePlan& plan, hipStream_t stream);
+
 hipError_t launch_write_kv(const WriteKvPlan& plan, hipStream_t stream);
 
 hipError_t launch_copy_blocks(const CopyBlocksPlan& plan, hipStream_t stream);

@@ -393,6 +393,77 @@ int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
   return PA_OK;
 }
 
+int plan_decode_lse(const pa_tensor* lse, const pa_tensor* q, const pa_tensor* k_pool,
+                    const pa_tensor* v_pool, const pa_tensor* out, DecodePlan* plan,
+                    std::string* err) {
+  int st = check_basic(lse, "lse", 2, err, true);
+  if (st) return st;
+  if (lse->dtype != PA_F32) return fail(err, PA_ERR_DTYPE, "lse must be f32");
+  if (lse->shape[0] != plan->S || lse->shape[1] != plan->H)
+    return fail(err, PA_ERR_SHAPE, "lse must be [%d, %d]", plan->S, plan->H);
+  if (lse->shape[1] > 1 && lse->stride[1] != 1)
+    return fail(err, PA_ERR_STRIDE, "lse: last dimension must be contiguous");
+  if (lse->data && (reinterpret_cast<uintptr_t>(lse->data) & 3u))
+    return fail(err, PA_ERR_STRIDE, "lse must be 4-byte aligned");
+  if (ranges_overlap(lse, q) || ranges_overlap(lse, k_pool) || ranges_overlap(lse, v_pool) ||
+      ranges_overlap(lse, out))
+    return fail(err, PA_ERR_ARG, "lse must not alias q, the pools or out");
+  plan->lse = static_cast<float*>(lse->data);
+  plan->lse_ss = lse->stride[0];
+  return PA_OK;
+}
+
+int plan_merge(const pa_tensor* part_out, const pa_tensor* part_lse, const pa_tensor* out,
+               const pa_tensor* lse, MergePlan* plan, std::string* err) {
+  int st;
+  if ((st = check_basic(part_out, "part_out", 4, err, true))) return st;
+  if ((st = check_basic(part_lse, "part_lse", 3, err, true))) return st;
+  if ((st = check_rows(out, "out", err))) return st;
+  if (part_out->dtype != PA_F32 || part_lse->dtype != PA_F32)
+    return fail(err, PA_ERR_DTYPE, "part_out and part_lse must be f32");
+  if (!is_float(out->dtype)) return fail(err, PA_ERR_DTYPE, "out must be f32, f16 or bf16");
+  const int64_t P = part_out->shape[0], S = part_out->shape[1], H = part_out->shape[2],
+                D = part_out->shape[3];
+  if (P < 1) return fail(err, PA_ERR_SHAPE, "at least one part is needed");
+  if (part_lse->shape[0] != P || part_lse->shape[1] != S || part_lse->shape[2] != H)
+    return fail(err, PA_ERR_SHAPE, "part_lse must be [%lld, %lld, %lld]", (long long)P,
+                (long long)S, (long long)H);
+  if (out->shape[0] != S || out->shape[1] != H || out->shape[2] != D)
+    return fail(err, PA_ERR_SHAPE, "out must be [%lld, %lld, %lld]", (long long)S,
+                (long long)H, (long long)D);
+  if (!(D == 64 || D == 128))
+    return fail(err, PA_ERR_UNSUPPORTED, "head size %lld (supported: 64, 128)", (long long)D);
+  if (D > 1 && part_out->stride[3] != 1)
+    return fail(err, PA_ERR_STRIDE, "part_out: last dimension must be contiguous");
+  if (P * S * H > ((int64_t)1 << 31) - 1)
+    return fail(err, PA_ERR_UNSUPPORTED, "too many parts");
+  if (lse) {
+    if ((st = check_basic(lse, "lse", 2, err, true))) return st;
+    if (lse->dtype != PA_F32) return fail(err, PA_ERR_DTYPE, "lse must be f32");
+    if (lse->shape[0] != S || lse->shape[1] != H)
+      return fail(err, PA_ERR_SHAPE, "lse must be [%lld, %lld]", (long long)S, (long long)H);
+    if (ranges_overlap(lse, part_out) || ranges_overlap(lse, part_lse) ||
+        ranges_overlap(lse, out))
+      return fail(err, PA_ERR_ARG, "lse must not alias the parts or out");
+  }
+  if (ranges_overlap(out, part_out) || ranges_overlap(out, part_lse))
+    return fail(err, PA_ERR_ARG, "out must not alias the parts");
+  MergePlan p;
+  p.P = (int)P; p.S = (int)S; p.H = (int)H; p.D = (int)D;
+  p.part_out = static_cast<const float*>(part_out->data);
+  p.po_p = part_out->stride[0]; p.po_s = part_out->stride[1]; p.po_h = part_out->stride[2];
+  p.part_lse = static_cast<const float*>(part_lse->data);
+  p.pl_p = part_lse->stride[0]; p.pl_s = part_lse->stride[1]; p.pl_h = part_lse->stride[2];
+  p.out = out->data; p.out_dtype = out->dtype;
+  p.o_s = out->stride[0]; p.o_h = out->stride[1];
+  if (lse) {
+    p.lse = static_cast<float*>(lse->data);
+    p.l_s = lse->stride[0]; p.l_h = lse->stride[1];
+  }
+  *plan = p;
+  return PA_OK;
+}
+
 int plan_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_tensor* src,
                      const pa_tensor* dst, CopyBlocksPlan* plan, std::string* err) {
   int st;

@@ -63,6 +63,10 @@ struct DecodePlan {
   int n_pre = 0;
   const float* pre_o = nullptr;
   const float* pre_lse = nullptr;
+  // Optional natural-log log-sum-exp of each (sequence, query head),
+  // lse[s * lse_ss + h] (pa_decode_lse).
+  float* lse = nullptr;
+  int64_t lse_ss = 0;
 };
 
 // Query positions per prefill workgroup (all G heads of one KV head).
@@ -119,6 +123,20 @@ struct WriteKvPlan {
   void* vp = nullptr;
 };
 
+// Merge of P partial attention states (pa_merge_states).
+struct MergePlan {
+  int P = 0, S = 0, H = 0, D = 0;
+  const float* part_out = nullptr;  // [P, S, H, D], strides in elements
+  int64_t po_p = 0, po_s = 0, po_h = 0;
+  const float* part_lse = nullptr;  // [P, S, H]
+  int64_t pl_p = 0, pl_s = 0, pl_h = 0;
+  void* out = nullptr;              // [S, H, D]
+  int out_dtype = 0;
+  int64_t o_s = 0, o_h = 0;
+  float* lse = nullptr;             // optional [S, H]
+  int64_t l_s = 0, l_h = 0;
+};
+
 struct CopyBlocksPlan {
   int64_t N = 0;           // block pairs
   int64_t block_bytes = 0; // bytes of one block in one pool
@@ -142,6 +160,15 @@ int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v
 int plan_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
                   const pa_tensor* slot_mapping, const pa_tensor* k_pool,
                   const pa_tensor* v_pool, WriteKvPlan* plan, std::string* err);
+
+// Checks the optional log-sum-exp output of pa_decode_lse: f32 [S, H],
+// not overlapping q, the pools or out.
+int plan_decode_lse(const pa_tensor* lse, const pa_tensor* q, const pa_tensor* k_pool,
+                    const pa_tensor* v_pool, const pa_tensor* out, DecodePlan* plan,
+                    std::string* err);
+
+int plan_merge(const pa_tensor* part_out, const pa_tensor* part_lse, const pa_tensor* out,
+               const pa_tensor* lse, MergePlan* plan, std::string* err);
 
 int plan_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_tensor* src,
                      const pa_tensor* dst, CopyBlocksPlan* plan, std::string* err);

@@ -226,3 +226,33 @@ def test_pool_layouts():
         head_major(t)
         t.stride[1], t.stride[2] = 2 * 128, 16 * 128  # rows of a head not adjacent
     assert call_decode(c) == -4
+
+
+def test_decode_lse_and_merge_reject():
+    """pa_decode_lse checks its lse output, pa_merge_states its parts, before
+    any GPU work."""
+    L = B.lib()
+    r = ctypes.byref
+    a = decode_args(S=4, H=32)
+    bad = [(T([4, 32], B.PA_F16, 7 * GAP), -2),            # not f32
+           (T([4, 31], B.PA_F32, 7 * GAP), -3),            # wrong shape
+           (T([4, 32], B.PA_F32, 7 * GAP, [1, 4]), -4),    # last dim not contiguous
+           (T([4, 32], B.PA_F32, 6 * GAP), -8)]            # aliases out
+    for lse, status in bad:
+        st = L.pa_decode_lse(r(a["q"]), r(a["k"]), r(a["v"]), r(a["bt"]), r(a["cl"]),
+                             ctypes.c_float(0.1), r(a["out"]), r(lse), None)
+        assert st == status, L.pa_last_error()
+    assert L.pa_decode_lse(r(a["q"]), r(a["k"]), r(a["v"]), r(a["bt"]), r(a["cl"]),
+                           ctypes.c_float(0.1), r(a["out"]), None, None) == -1
+    P, S, H, d = 3, 4, 8, 128
+    po, pl = T([P, S, H, d], B.PA_F32, GAP), T([P, S, H], B.PA_F32, 2 * GAP)
+    out = T([S, H, d], B.PA_BF16, 3 * GAP)
+    cases = [(T([P, S, H, d], B.PA_F16, GAP), pl, out, -2),
+             (po, T([P, S, H + 1], B.PA_F32, 2 * GAP), out, -3),
+             (po, pl, T([S, H, 64], B.PA_F32, 3 * GAP), -3),
+             (T([P, S, H, 96], B.PA_F32, GAP), pl, T([S, H, 96], B.PA_F32, 3 * GAP), -5),
+             (T([0, S, H, d], B.PA_F32, GAP), T([0, S, H], B.PA_F32, 2 * GAP), out, -3),
+             (po, pl, T([S, H, d], B.PA_F32, GAP + 64), -8)]
+    for po_, pl_, out_, status in cases:
+        st = L.pa_merge_states(r(po_), r(pl_), r(out_), None, None)
+        assert st == status, L.pa_last_error()
