@@ -64,9 +64,10 @@ def parse():
                          "profiles/<KERNEL>_<WORKLOAD>_traffic.json (no GPU needed)")
     ap.add_argument("--only", default="",
                     help="comma list of workloads to run (for profiling): "
-                         "gqa,long,gqa-hm,long-hm,prefix,prefill; prefix16 runs the "
-                         "prefix-shared workload at B = 16 only; -hm: pools head-major "
-                         "within blocks")
+                         "gqa,long,gqa-hm,long-hm,share,prefix,prefill,copy; prefix16 runs "
+                         "the prefix-shared workload at B = 16 only; -hm: pools head-major "
+                         "within blocks; share: one eighth of the long context and the "
+                         "merge of eight partial states")
     return ap.parse_args()
 
 
@@ -225,6 +226,52 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
                 prefix_ms=pre_ms if pre_n else 0.0)
 
 
+def bench_long_share(torch, binding, W, steps):
+    """The long-context workload split eight ways by contiguous block ranges
+    (the split across GPUs that pa_decode_lse + pa_merge_states serve): one
+    range's pa_decode_lse and the merge of eight such partial states, timed
+    by the library's kernel timer."""
+    import numpy as np
+    case = W.long_bf16_decode()
+    B = case.block_size
+    b1 = round(-(-int(case.context_lens.max()) // B) / 8)
+    table = np.ascontiguousarray(case.block_table[:, :b1])
+    lens = np.minimum(case.context_lens, b1 * B).astype(np.int32)
+    share = W.PagedCase(case.dtype, case.q, case.k_pool, case.v_pool, table, lens, case.scale)
+    nbytes = W.decode_bytes(share, out_bytes_per_elem=4)
+    d = binding.upload_case(share)
+    S, H, D = case.q.shape
+    out = torch.empty((S, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    parts = torch.randn((8, S, H, D), dtype=torch.float32, device="cuda")
+    part_lse = torch.randn((8, S, H), dtype=torch.float32, device="cuda")
+    merged = torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda")
+    call = lambda: binding.decode_lse(d["q"], d["k_pool"], d["v_pool"], d["block_table"],  # noqa
+                                      d["context_lens"], case.scale, out=out, lse=lse)
+    for _ in range(3):
+        call()
+        binding.merge_states(parts, part_lse, out=merged, want_lse=False)
+    torch.cuda.synchronize()
+    binding.profiler_reset()
+    binding.profiler_enable(True)
+    for _ in range(steps):
+        call()
+        binding.merge_states(parts, part_lse, out=merged, want_lse=False)
+    torch.cuda.synchronize()
+    binding.profiler_enable(False)
+    dec_ms, _ = kernel_avg_ms(binding, "decode_partitions")
+    mrg_ms, _ = kernel_avg_ms(binding, "merge_states")
+    binding.profiler_reset()
+    del d, out, lse, parts, part_lse, merged
+    binding.workspace_release()
+    torch.cuda.empty_cache()
+    return {"keys_per_sequence": int(lens.max()),
+            "share_decode_kernel_avg_us": round(dec_ms * 1e3, 2),
+            "share_decode_kernel_GB/s": round(nbytes / (dec_ms * 1e-3) / 1e9, 1),
+            "merge_8_parts_kernel_avg_us": round(mrg_ms * 1e3, 2),
+            "algorithmic_bytes_share": nbytes}
+
+
 def copy_bandwidth(torch, reps=10):
     """Attainable HBM rate for context: a 1 GiB device-to-device copy (1 GiB
     read + 1 GiB written per call), wall clock over `reps` calls."""
@@ -374,6 +421,10 @@ def main():
                 "partition_kernel_avg_us": round(rh["part_ms"] * 1e3, 2),
                 "pool_layout": "[NB, Hkv, B, d] memory, viewed as [NB, B, Hkv, d]"}
             del case
+        # ---- one GPU's share of the long context split eight ways ----------
+        if want("share"):
+            extra["long-bf16-decode-8way-share"] = bench_long_share(torch, binding, W,
+                                                                    max(10, a.steps // 2))
         # ---------------- prefix-shared decode sweep ---------------------
         if want("prefix") or want("prefix16"):
             for B in ((16, 32, 64, 128) if want("prefix") else (16,)):

@@ -938,14 +938,25 @@ __global__ __launch_bounds__(256) void merge_states_kernel(MergeArgs a) {
 #pragma unroll
   for (int e = 0; e < kV; ++e) acc[e] = 0.f;
   if (M != -INFINITY) {
+    // Four parts' loads in flight together; parts past P enter as empty.
     const float* op = a.po + (int64_t)s * a.po_s + (int64_t)h * a.po_h + lane * kV;
-    for (int p = 0; p < a.P; ++p) {
-      const float l = lp[(int64_t)p * a.pl_p];
-      if (l == -INFINITY) continue;
-      const float w = fast_exp2((l - M) * 1.4426950408889634f);
-      wsum += w;
+    for (int p0 = 0; p0 < a.P; p0 += 4) {
+      float l[4], o[4][kV];
 #pragma unroll
-      for (int e = 0; e < kV; ++e) acc[e] = fmaf(w, op[(int64_t)p * a.po_p + e], acc[e]);
+      for (int u = 0; u < 4; ++u) {
+        const bool in = p0 + u < a.P;
+        l[u] = in ? lp[(int64_t)(p0 + u) * a.pl_p] : -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kV; ++e) o[u][e] = in ? op[(int64_t)(p0 + u) * a.po_p + e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (l[u] == -INFINITY) continue;
+        const float w = fast_exp2((l[u] - M) * 1.4426950408889634f);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < kV; ++e) acc[e] = fmaf(w, o[u][e], acc[e]);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
