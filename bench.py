@@ -71,9 +71,14 @@ def parse():
     return ap.parse_args()
 
 
+# Headers every kernel source includes; a change in any of them can change
+# the compiled kernels, so they enter every kernel's source hash.
+SHARED_HEADERS = ("device_common.h", "kernels.h", "launch.h", "plan.h")
+
+
 def source_hash(*names):
     h = hashlib.sha256()
-    for n in names:
+    for n in (*names, *SHARED_HEADERS):
         with open(os.path.join(ROOT, "paged_kv_cache_decode_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
