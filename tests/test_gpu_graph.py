@@ -198,3 +198,80 @@ def test_shared_prefix_graph_replays(pa):
         torch.cuda.synchronize()
         assert torch.equal(out_g, eager), f"replay {i}"
     pa.workspace_release(s)
+
+
+def test_context_split_graph_replays(pa):
+    """Two key ranges decoded with pa_decode_lse into slices of one buffer and
+    joined with pa_merge_states, captured once and replayed."""
+    from tests.test_gpu_context_split import split_by_blocks
+    c = W.make_decode_case(805, 10, 32, 8, 128, 16, "bf16", len_range=(1, 1500))
+    dev = case_to_dev(c)
+    parts = [(to_dev(t), to_dev(n)) for t, n in split_by_blocks(c, [0, 40, 200])]
+    S, H, d = c.q.shape
+    part_out = torch.empty((2, S, H, d), dtype=torch.float32, device="cuda")
+    part_lse = torch.empty((2, S, H), dtype=torch.float32, device="cuda")
+
+    def step(out, lse):
+        for p, (tab, lens) in enumerate(parts):
+            pa.decode_lse(dev["q"], dev["k_pool"], dev["v_pool"], tab, lens, c.scale,
+                          out=part_out[p], lse=part_lse[p])
+        pa.merge_states(part_out, part_lse, out=out, lse=lse)
+
+    out_g = torch.empty((S, H, d), dtype=torch.float32, device="cuda")
+    lse_g = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step(out_g, lse_g)  # sizes this stream's workspace
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(out_g, lse_g)
+    for i in range(3):
+        qi = new_q(c, 910 + i)
+        dev["q"].copy_(to_dev(qi, c.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        out_e, lse_e = torch.empty_like(out_g), torch.empty_like(lse_g)
+        step(out_e, lse_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {i}"
+        assert torch.equal(lse_g, lse_e), f"replay {i} lse"
+    ref, ref_lse = oracle.decode(qi, c.k_pool, c.v_pool, c.block_table, c.context_lens,
+                                 c.scale, c.dtype)
+    assert_close_f32_out(out_to_f64(out_g), ref, c.dtype, "last replay vs oracle")
+    assert np.abs(lse_g.cpu().numpy() - ref_lse).max() <= 1e-4
+    pa.workspace_release(s)
+
+
+def test_shared_prefix_graph_replays(pa):
+    """pa_decode_shared_prefix (prefix step, then the suffix decode that
+    merges it) captured once and replayed."""
+    B, prefix = 16, 256
+    c = W.make_prefix_shared_case(806, B, num_seqs=24, prefix_len=prefix,
+                                  suffix_range=(0, 300), num_heads=32, num_kv_heads=8,
+                                  dtype="bf16")
+    dev = case_to_dev(c)
+    args = lambda: (dev["q"], dev["k_pool"], dev["v_pool"], dev["block_table"],
+                    dev["context_lens"], prefix, c.scale)
+    s = torch.cuda.Stream()
+    out_g = torch.empty(dev["q"].shape, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        pa.decode_shared_prefix(*args(), out=out_g)  # sizes this stream's workspace
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pa.decode_shared_prefix(*args(), out=out_g)
+    for i in range(3):
+        qi = new_q(c, 920 + i)
+        dev["q"].copy_(to_dev(qi, c.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = pa.decode_shared_prefix(*args(), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, eager), f"replay {i}"
+    ref, _ = oracle.decode(qi, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale,
+                           c.dtype)
+    assert_close_f32_out(out_to_f64(out_g), ref, c.dtype, "last replay vs oracle")
+    pa.workspace_release(s)
