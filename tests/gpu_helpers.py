@@ -42,42 +42,82 @@ def out_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+# Worst max-abs error seen per named workload in this session (written to
+# the file named by PA_PARITY_REPORT at the end of the session).
+MAX_ABS = {}
+
+
+def record_max_abs(name: str, worst: float):
+    MAX_ABS[name] = max(MAX_ABS.get(name, 0.0), float(worst))
+
+
 def assert_close_f32_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "",
-                         factor: float = 1.0):
-    """Max-abs check against TOL[dtype] * factor (factor > 1 only for scores
-    larger than the standard scale gives; see score_factor)."""
-    tol = TOL[dtype] * factor
+                         extra: np.ndarray | float = 0.0, record: str | None = None):
+    """Max-abs check against TOL[dtype], plus an optional additive,
+    per-element term ``extra`` (see f32_score_rounding_bound).  Returns the
+    largest error; with ``record`` it is also kept under that name."""
+    bound = TOL[dtype] + np.asarray(extra, dtype=np.float64)
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     worst = float(err.max()) if err.size else 0.0
-    assert worst <= tol, f"{what}: max-abs error {worst:.3e} > {tol:.1e}"
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} outputs beyond the bound, max-abs error "
+                           f"{worst:.3e}, worst excess {float((err - bound).max()):.3e} "
+                           f"(TOL {TOL[dtype]:.1e})")
+    if record:
+        record_max_abs(record, worst)
     return worst
 
 
-def score_factor(c) -> float:
-    """How far a decode case's scaled scores exceed the standard range.
+U32 = 2.0 ** -24  # unit roundoff of fp32
 
-    The kernels compute the scores s * scale in fp32, so their rounding error
-    grows with |s * scale|; the tolerances above hold for the standard
-    1/sqrt(d) scale on unit-normal data, where |s * scale| stays below about
-    4.  This returns max(1, X / 4), X = the largest |s * scale| over the
-    case's attended keys (computed in fp64 from the stored inputs)."""
+
+def f32_score_rounding_bound(c) -> np.ndarray:
+    """Additive first-order bound on what forming the scores in fp32 adds to
+    a decode output, for a case with fp32 inputs, per element [S, H, d].
+
+    The kernel forms y_t = scale * (q . k_t) by an fp32 dot product of d
+    terms and exponentiates y_t - max in fp32.  With u = 2^-24:
+      |error of q . k_t| <= gamma_d * A_t,   gamma_d = d u / (1 - d u),
+                                           A_t = sum_i |q_i k_ti|;
+      multiplying by the rounded scale * log2(e) adds <= 2u |y_t|;
+      the subtraction of the maximum adds <= u |y_t - y_max|;
+      the exponential adds <= 2^-22 (relative).
+    So each weight p_t carries a relative error
+      eps_t <= |scale| gamma_d A_t + 2u |y_t| + u |y_t - y_max| + 2^-22,
+    and, because the output normalises by the sum of the same weights,
+      |delta o_j| <= sum_t p_t eps_t |v_tj - o_j|   (to first order).
+    A common shift of every y_t (the maximum's own error) cancels in that
+    normalisation.  The term grows with the scores' size: it is about 1e-6
+    at the standard scale 1/sqrt(d) on unit-normal data, and it is what a
+    large scale (|y| of order 100) adds to the 1e-5 of the fp32 inputs."""
+    import oracle
     from oracle.dtypes import to_f64
     q = to_f64(c.q, c.dtype)
-    k = to_f64(c.k_pool, c.dtype)
-    S, H, _ = q.shape
-    Hkv, B = k.shape[2], k.shape[1]
+    kp = to_f64(c.k_pool, c.dtype)
+    vp = to_f64(c.v_pool, c.dtype)
+    S, H, d = q.shape
+    B, Hkv = kp.shape[1], kp.shape[2]
     G = H // Hkv
-    x_max = 0.0
+    gamma = d * U32 / (1.0 - d * U32)
+    out = np.zeros((S, H, d))
     for s in range(S):
         n = int(c.context_lens[s])
         if n == 0:
             continue
         t = np.arange(n)
-        rows = k[c.block_table[s, t // B].astype(np.int64), t % B]  # [n, Hkv, d]
+        blk = c.block_table[s, t // B].astype(np.int64)
         for h in range(H):
-            x_max = max(x_max, float(np.abs(rows[:, h // G] @ q[s, h]).max()) * abs(c.scale))
-    return max(1.0, x_max / 4.0)
+            k = kp[blk, t % B, h // G]
+            v = vp[blk, t % B, h // G]
+            o, _, p = oracle.decode_row(c.q, c.k_pool, c.v_pool, c.block_table,
+                                        c.context_lens, c.scale, c.dtype, s, h)
+            y = c.scale * (k @ q[s, h])
+            a = np.abs(k) @ np.abs(q[s, h])
+            eps = abs(c.scale) * gamma * a + 2 * U32 * np.abs(y) + U32 * np.abs(y - y.max()) \
+                + 2.0 ** -22
+            out[s, h] = (p * eps) @ np.abs(v - o)
+    return out
 
 
 def assert_close_native_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):

@@ -40,7 +40,7 @@ def oracle_decode(c):
 def test_tiny_f32_decode(pa):
     c = W.tiny_f32_decode()
     got = out_to_f64(run_decode(pa, c))
-    assert_close_f32_out(got, oracle_decode(c), "f32", "tiny-f32-decode")
+    assert_close_f32_out(got, oracle_decode(c), "f32", "tiny-f32-decode", record="tiny-f32-decode")
 
 
 EDGE_LENS = [0, 1, 15, 16, 17, 63, 64, 65, 100, 257, 1000, 1537]
@@ -212,39 +212,20 @@ def test_gqa_f16_decode_full(pa):
     ref = oracle_decode(c)
     dev = case_to_dev(c)
     got = out_to_f64(run_decode(pa, c, dev=dev))
-    worst = assert_close_f32_out(got, ref, "f16", "gqa-f16-decode")
+    worst = assert_close_f32_out(got, ref, "f16", "gqa-f16-decode", record="gqa-f16-decode")
     print(f"gqa-f16-decode max-abs {worst:.2e}")
     nat = out_to_f64(run_decode(pa, c, out_dtype=torch.float16, dev=dev))
     assert_close_native_out(nat, ref, "f16", "gqa-f16-decode native")
 
 
-@pytest.mark.slow
-def test_long_bf16_decode_sampled(pa):
-    """4 x 100,000 keys, bf16: sampled (sequence, head) outputs vs the oracle."""
-    c = W.long_bf16_decode()
-    dev = case_to_dev(c)
-    got = out_to_f64(run_decode(pa, c, dev=dev))
-    rng = np.random.default_rng(9)
-    for s in range(c.num_seqs):
-        for h in rng.choice(32, size=3, replace=False):
-            ref, _, _ = oracle.decode_row(c.q, c.k_pool, c.v_pool, c.block_table,
-                                          c.context_lens, c.scale, c.dtype, s, int(h))
-            assert_close_f32_out(got[s, h], ref, "bf16", f"long s={s} h={h}")
-
-
 @pytest.mark.parametrize("B", [16, 32, 64, 128])
-def test_prefix_shared_decode_sampled(pa, B):
-    """256 sequences sharing a 2048-token prefix: sampled outputs, and the
-    shared table gives the same bits as private copies of the prefix."""
+def test_prefix_shared_tables_match_private_copies(pa, B):
+    """256 sequences sharing a 2048-token prefix: for the first 16, tables
+    that point at the shared blocks give the same bits as tables that point
+    at private copies of the prefix (every output of the workload is checked
+    against the oracle in test_gpu_full_configs.py)."""
     c = W.prefix_shared_bf16_decode(B)
     dev = case_to_dev(c)
-    got = out_to_f64(run_decode(pa, c, dev=dev))
-    rng = np.random.default_rng(B)
-    for s in rng.choice(c.num_seqs, size=6, replace=False):
-        for h in rng.choice(32, size=2, replace=False):
-            ref, _, _ = oracle.decode_row(c.q, c.k_pool, c.v_pool, c.block_table,
-                                          c.context_lens, c.scale, c.dtype, int(s), int(h))
-            assert_close_f32_out(got[s, h], ref, "bf16", f"prefix B={B} s={s} h={h}")
     # Private copies of the prefix for the first 16 sequences.
     S = 16
     nsh = c.meta["shared_blocks"]

@@ -78,23 +78,6 @@ def test_prefill_last_row_matches_decode(pa):
     assert (pre[last] - dec).abs().max().item() <= 2e-3
 
 
-def test_causal_bf16_prefill_sampled(pa):
-    """8 prompts of 512..4096 tokens, 32/8 heads, bf16, causal: sampled rows,
-    including the first and last rows of every prompt."""
-    c = W.causal_bf16_prefill()
-    got = out_to_f64(run_prefill(pa, c))
-    rng = np.random.default_rng(4)
-    rows = []
-    qsl = c.query_start_loc
-    for s in range(c.num_seqs):
-        for t in (qsl[s], qsl[s + 1] - 1, *rng.integers(qsl[s], qsl[s + 1], size=6)):
-            rows.append((int(t), int(rng.integers(0, 32))))
-    ref, _ = oracle.prefill_rows(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, qsl,
-                                 c.scale, True, c.dtype, rows)
-    for r, (t, h) in enumerate(rows):
-        assert_close_f32_out(got[t, h], ref[r], "bf16", f"row {t} head {h}")
-
-
 def test_prefill_many_prompts(pa):
     """90 prompts, mostly short (the padded grid then holds far more empty
     query-tile slots than real ones), some continuing a longer context:

@@ -14,7 +14,7 @@ import torch
 import oracle
 from paged_kv_cache_decode_amd import workloads as W
 from tests.gpu_helpers import (assert_close_f32_out, assert_close_native_out, case_to_dev,
-                               out_to_f64, score_factor)
+                               f32_score_rounding_bound, out_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,10 @@ def test_decode_random_configs(pa, monkeypatch, seed):
     got = pa.decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_table"],
                     dev["context_lens"], c.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert_close_f32_out(out_to_f64(got), ref, dtype, what, factor=score_factor(c))
+    # 16-bit inputs: 2e-3 at every drawn scale.  fp32 inputs: 1e-5 plus the
+    # derived effect of forming large scores in fp32.
+    extra = f32_score_rounding_bound(c) if dtype == "f32" else 0.0
+    assert_close_f32_out(out_to_f64(got), ref, dtype, what, extra=extra)
     if dtype != "f32":
         nat = pa.decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_table"],
                         dev["context_lens"], c.scale)
