@@ -27,7 +27,13 @@ struct pa_block_manager {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
   std::vector<int32_t> free_list;  // stack; back() is handed out next
-  std::vector<int32_t> refcount;   // per physical block
+  std::vector<int32_t> refcount;   // per physical block: sequences holding it
+  // Per physical block: queued copy pairs that name it (as source or
+  // destination).  A block returns to the free list only when no sequence
+  // holds it and no queued pair names it, so the blocks of a queued pair
+  // cannot be handed out again before the caller has taken the pair.
+  std::vector<int32_t> pending;
+  std::vector<uint8_t> pending_dst;  // 1 while the block is a queued destination
   struct Seq {
     std::vector<int32_t> blocks;  // logical block j -> physical block
     int64_t tokens = 0;
@@ -50,8 +56,13 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
+void maybe_free(pa_block_manager* bm, int32_t b) {
+  if (bm->refcount[b] == 0 && bm->pending[b] == 0) bm->free_list.push_back(b);
+}
+
 void release_block(pa_block_manager* bm, int32_t b) {
-  if (--bm->refcount[b] == 0) bm->free_list.push_back(b);
+  --bm->refcount[b];
+  maybe_free(bm, b);
 }
 
 }  // namespace
@@ -76,6 +87,8 @@ pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size) {
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
   bm->refcount.assign(num_blocks, 0);
+  bm->pending.assign(num_blocks, 0);
+  bm->pending_dst.assign(num_blocks, 0);
   bm->free_list.reserve(num_blocks);
   for (int32_t b = num_blocks - 1; b >= 0; --b) bm->free_list.push_back(b);  // 0 first
   return bm;
@@ -127,6 +140,10 @@ int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int32_t n, int32_t* slots
   const int64_t need = (sq.tokens + n + B - 1) / B;       // blocks after the append
   const bool partial_last = sq.tokens % B != 0;
   const bool cow = n > 0 && partial_last && bm->refcount[sq.blocks[used - 1]] > 1;
+  if (cow && bm->pending_dst[sq.blocks[used - 1]])
+    return fail(PA_ERR_ARG, "sequence %lld: its last block %d is the destination of a queued "
+                "copy and must be copied again; take and run the queued copies (and write "
+                "the tokens appended so far) first", (long long)seq_id, sq.blocks[used - 1]);
   const int64_t fresh = (need - used) + (cow ? 1 : 0);
   if (fresh > (int64_t)bm->free_list.size())
     return fail(PA_ERR_ALLOC, "sequence %lld needs %lld free blocks, %zu left",
@@ -140,6 +157,10 @@ int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int32_t n, int32_t* slots
     bm->refcount[nb] = 1;
     --bm->refcount[old];  // still > 0: another sequence holds it
     sq.blocks[used - 1] = nb;
+    // The queued pair keeps both blocks out of the free list until taken.
+    ++bm->pending[old];
+    ++bm->pending[nb];
+    bm->pending_dst[nb] = 1;
     bm->copy_src.push_back(old);
     bm->copy_dst.push_back(nb);
   }
@@ -166,6 +187,14 @@ int pa_bm_take_copies(pa_block_manager* bm, int32_t* src, int32_t* dst, int32_t 
   if (k > 0 && (!src || !dst)) return fail(PA_ERR_NULL, "src or dst is NULL");
   std::copy(bm->copy_src.begin(), bm->copy_src.begin() + k, src);
   std::copy(bm->copy_dst.begin(), bm->copy_dst.begin() + k, dst);
+  for (int32_t i = 0; i < k; ++i) {
+    const int32_t a = bm->copy_src[i], b = bm->copy_dst[i];
+    bm->pending_dst[b] = 0;
+    --bm->pending[a];
+    --bm->pending[b];
+    maybe_free(bm, a);
+    maybe_free(bm, b);
+  }
   bm->copy_src.erase(bm->copy_src.begin(), bm->copy_src.begin() + k);
   bm->copy_dst.erase(bm->copy_dst.begin(), bm->copy_dst.begin() + k);
   return k;

@@ -88,9 +88,11 @@ def f32_score_rounding_bound(c) -> np.ndarray:
     and, because the output normalises by the sum of the same weights,
       |delta o_j| <= sum_t p_t eps_t |v_tj - o_j|   (to first order).
     A common shift of every y_t (the maximum's own error) cancels in that
-    normalisation.  The term grows with the scores' size: it is about 1e-6
-    at the standard scale 1/sqrt(d) on unit-normal data, and it is what a
-    large scale (|y| of order 100) adds to the 1e-5 of the fp32 inputs."""
+    normalisation.  The term is a worst-case bound (every rounding error
+    taken with the same sign) and grows with the scores' size: about 2e-5
+    at the standard scale 1/sqrt(d) on unit-normal data (where the
+    workloads' fixed 1e-5 applies instead) and up to about 1e-3 at a scale
+    of 0.5 or 2 with d = 128."""
     import oracle
     from oracle.dtypes import to_f64
     q = to_f64(c.q, c.dtype)

@@ -187,3 +187,140 @@ def test_random_scenario_attention_matches_dense():
             p = np.exp(x - x.max())
             ref = (p / p.sum()) @ V[:, h // G]
             assert np.allclose(paged[i, h], ref, rtol=0, atol=1e-12)
+
+
+def test_queued_copy_keeps_its_source_out_of_the_free_list():
+    """A shared partial block X is copied for sequence 1 (pair X -> Y
+    queued); its other holder is freed before the pair is taken.  X must not
+    return to the free list while the pair waits, so a second copy-on-write
+    in the same batch cannot be handed X as its fresh destination (which
+    would make one batch copy into X and out of X at once)."""
+    bm = B.BlockManager(8, 4)
+    bm.add(0)
+    bm.append(0, 2)                 # X, 2 of 4 slots used
+    x = int(bm.block_table([0], 1)[0][0, 0])
+    bm.fork(0, 1)
+    bm.append(1, 1)                 # X shared and partial: X -> Y queued
+    free_before = bm.num_free
+    bm.free(0)                      # X's last holder leaves; the pair still names X
+    assert bm.num_free == free_before and bm.refcount(x) == 0
+    bm.add(3)
+    bm.append(3, 2)
+    bm.fork(3, 4)
+    bm.append(4, 1)                 # a second copy-on-write in the same batch
+    src, dst = bm.take_copies()
+    assert len(src) == 2
+    assert not set(src.tolist()) & set(dst.tolist()) and len(set(dst.tolist())) == 2
+    assert x not in dst.tolist()
+    # Sequence 3's block and the second copy's destination were taken; X was
+    # freed when its pair was taken.
+    assert bm.num_free == free_before - 2 + 1
+    bm.free(1)
+    bm.free(3)
+    bm.free(4)
+    assert bm.num_free == 8
+
+
+def test_copy_of_a_queued_destination_is_refused():
+    """A block that is the destination of a queued pair holds no copied data
+    yet; copying it again in the same batch is refused, state unchanged, and
+    allowed once the queue has been taken."""
+    bm = B.BlockManager(8, 4)
+    bm.add(0)
+    bm.append(0, 2)
+    bm.fork(0, 1)
+    bm.append(1, 1)                 # X -> Y queued; sequence 1 now holds Y
+    bm.fork(1, 2)                   # Y shared by 1 and 2 while still a queued destination
+    before = (bm.num_free, bm.block_table([1, 2], 2))
+    with pytest.raises(B.PAError) as e:
+        bm.append(2, 1)
+    assert e.value.status == -8
+    after = (bm.num_free, bm.block_table([1, 2], 2))
+    assert before[0] == after[0] and (before[1][0] == after[1][0]).all()
+    assert (before[1][1] == after[1][1]).all()
+    src, dst = bm.take_copies()
+    assert len(src) == 1
+    y = int(dst[0])
+    bm.append(2, 1)                 # now Y -> Z is queued
+    src2, dst2 = bm.take_copies()
+    assert list(src2) == [y] and int(dst2[0]) != y
+
+
+@pytest.mark.parametrize("seed", [4, 5, 6, 7])
+def test_batched_copies_are_independent(seed):
+    """Random adds / appends / forks / frees with the copy queue taken only
+    every few operations, following the documented order of work (run a
+    batch's copies, then write the tokens of the appends before it; write
+    pending tokens before a fork).  Every batch is a set of independent
+    pairs, and the final tables gather every sequence's logical tokens."""
+    rng = np.random.default_rng(seed)
+    NB, Bs, Hkv, d = 40, 4, 1, 4
+    bm = B.BlockManager(NB, Bs)
+    kp = np.full((NB, Bs, Hkv, d), np.nan, np.float32)
+    logical = {}
+    writes = []  # (seq, slots, rows) appended since the last flush
+    next_id = 0
+
+    def flush():
+        src, dst = bm.take_copies()
+        assert not set(src.tolist()) & set(dst.tolist()), (src, dst)
+        assert len(set(dst.tolist())) == len(dst)
+        for a_, b_ in zip(src, dst):
+            kp[b_] = kp[a_]
+        for sid, slots, rows in writes:
+            if sid in logical:  # a freed sequence's tokens are dropped
+                for x, r in zip(slots, rows):
+                    kp[x // Bs, x % Bs] = r
+        writes.clear()
+
+    for step in range(300):
+        op = rng.integers(0, 5)
+        if op == 0 or not logical:
+            bm.add(next_id)
+            logical[next_id] = []
+            next_id += 1
+        elif op in (1, 2):
+            sid = int(rng.choice(list(logical)))
+            n = int(rng.integers(1, 6))
+            try:
+                slots = bm.append(sid, n)
+            except B.PAError as e:
+                if e.status == -8:      # copy of a queued destination: flush, retry
+                    flush()
+                    try:
+                        slots = bm.append(sid, n)
+                    except B.PAError as e2:
+                        assert e2.status == -6
+                        continue
+                else:
+                    assert e.status == -6
+                    continue
+            rows = rng.standard_normal((n, Hkv, d)).astype(np.float32)
+            writes.append((sid, slots, rows))
+            logical[sid].extend(rows)
+        elif op == 3:
+            sid = int(rng.choice(list(logical)))
+            flush()  # the child shares the parent's slots: write them first
+            bm.fork(sid, next_id)
+            logical[next_id] = list(logical[sid])
+            next_id += 1
+        else:
+            sid = int(rng.choice(list(logical)))
+            bm.free(sid)
+            del logical[sid]
+        if rng.random() < 0.2:
+            flush()
+    flush()
+    ids = sorted(logical)
+    table, lens = bm.block_table(ids, NB)
+    held = {}
+    for row, sid in zip(table, ids):
+        n = len(logical[sid])
+        assert lens[ids.index(sid)] == n
+        for b in row[:-(-n // Bs)]:
+            held[int(b)] = held.get(int(b), 0) + 1
+        if n:
+            t = np.arange(n)
+            assert np.array_equal(kp[row[t // Bs], t % Bs], np.stack(logical[sid]))
+    assert bm.num_free + len(held) == NB
+    assert all(bm.refcount(b) == c for b, c in held.items())
