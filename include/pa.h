@@ -60,8 +60,14 @@
  *     graph and replayed (a replay reads the buffers' contents at replay
  *     time).  A decode call that would have to grow its stream's workspace
  *     during a capture returns PA_ERR_ALLOC instead: make one call of the
- *     same (or larger) size on that stream before capturing.  Dispatches
- *     recorded into a graph are not timed by the profiler.
+ *     same (or larger) size on that stream before capturing.  A graph uses
+ *     the workspace of the stream it was captured on: a later call that
+ *     grows that workspace keeps the captured buffer alive (it is freed by
+ *     pa_workspace_release, which therefore invalidates such graphs), and
+ *     a replay must not overlap another call that uses the same workspace
+ *     (an eager decode on the capture stream, or a replay of another graph
+ *     captured on it).  Dispatches recorded into a graph are not timed by
+ *     the profiler.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -133,10 +139,11 @@ typedef struct pa_tensor {
  * more: about (W + S*Hkv) * G * (d + 1) * 4 + S * Hkv * 4 bytes (per-unit
  * counters, which the kernel leaves at zero, then partial results).  Growing
  * allocates (hipMallocAsync), zeroes the counters (hipMemsetAsync) and frees
- * the old buffer (hipFreeAsync), all on `stream`.  Calls on one stream
- * share the buffer safely; calls on different streams use different
- * buffers.  Release a stream's buffer with pa_workspace_release before
- * destroying the stream.
+ * the old buffer (hipFreeAsync), all on `stream` (a buffer that a graph
+ * captured on the stream uses is kept instead; see "Graph capture" above).
+ * Calls on one stream share the buffer safely; calls on different streams
+ * use different buffers.  Release a stream's buffer with
+ * pa_workspace_release before destroying the stream.
  * Returns PA_OK or a negative pa_status.
  */
 int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
@@ -295,7 +302,8 @@ int pa_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_te
  * pa_bm_create(num_blocks, block_size)  -- NULL on invalid sizes or no memory
  * pa_bm_destroy(bm)
  * pa_bm_num_free(bm)                    -- free blocks
- * pa_bm_refcount(bm, block)             -- sequences holding `block`
+ * pa_bm_refcount(bm, block)             -- sequences holding `block` (queued
+ *                                          copies do not count)
  * pa_bm_add(bm, seq_id)                 -- new empty sequence (id >= 0)
  * pa_bm_fork(bm, parent, child)         -- child shares all of parent's
  *                                          blocks and tokens
@@ -305,9 +313,18 @@ int pa_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_te
  *     If the sequence's last, partly filled block is shared, it is first
  *     replaced by a fresh block and the pair (old, fresh) is queued: the
  *     caller copies it (pa_copy_blocks) before writing the new tokens.
- *     PA_ERR_ALLOC when too few blocks are free; the sequence is unchanged.
- * pa_bm_take_copies(bm, src, dst, max)  -- moves up to max queued pairs out,
- *                                          returns how many
+ *     PA_ERR_ALLOC when too few blocks are free; PA_ERR_ARG when that shared
+ *     block is itself the destination of a pair still queued (take and run
+ *     the queued copies, and write the tokens appended so far, first).  On
+ *     any error the sequence is unchanged.
+ * pa_bm_take_copies(bm, src, dst, max)  -- moves up to max queued pairs out
+ *     in queue order and returns how many.  A queued pair keeps both of its
+ *     blocks out of the free list until it is taken, so no block of one
+ *     batch is the source or destination of another pair of the same batch:
+ *     a batch can run as one pa_copy_blocks call.  Order of work for the
+ *     caller: run the copies, then write the tokens of the appends whose
+ *     slots it holds; a sequence forked after an append shares that
+ *     append's slots, so write them before forking.
  * pa_bm_free(bm, seq_id)                -- releases the sequence
  * pa_bm_block_table(bm, seq_ids, S, MB, table, lens)
  *     host int32 table[S * MB] (row s: the blocks of seq_ids[s], then -1)
@@ -329,9 +346,11 @@ int pa_bm_block_table(pa_block_manager* bm, const int64_t* seq_ids, int32_t S, i
 
 /*
  * pa_workspace_release -- frees (stream-ordered, hipFreeAsync) the decode
- * workspace kept for `stream` on the current device.  Later pa_decode calls
- * on that stream allocate a new one.  Returns PA_OK (also when the stream
- * has none) or PA_ERR_LAUNCH.
+ * workspace kept for `stream` on the current device, including buffers that
+ * graphs captured on the stream still referenced after the workspace grew:
+ * graphs holding decode calls captured on `stream` must not be replayed
+ * afterwards.  Later pa_decode calls on that stream allocate a new one.
+ * Returns PA_OK (also when the stream has none) or PA_ERR_LAUNCH.
  */
 int pa_workspace_release(void* stream);
 

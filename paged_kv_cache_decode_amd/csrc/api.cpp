@@ -156,11 +156,15 @@ namespace {
 // the kernel resets every counter it uses) followed by the partial outputs.
 // Calls on one stream run in order, so they can share the buffer; a grown
 // buffer is allocated, its counters zeroed and the old one freed, all
-// stream-ordered on that stream.
+// stream-ordered on that stream -- unless a graph captured on the stream
+// holds the old buffer's address: such a buffer is kept (retired) until
+// pa_workspace_release, so that the graph's replays keep working.
 struct StreamWorkspace {
   void* ptr = nullptr;
   int64_t counter_bytes = 0;  // capacity of the counter region
   int64_t part_bytes = 0;     // capacity of the partial-result region
+  bool captured = false;      // a capture on this stream recorded `ptr`
+  std::vector<void*> retired; // superseded buffers that captured graphs use
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, void*>, StreamWorkspace> g_ws;
@@ -194,11 +198,18 @@ int acquire_workspace(pa::DecodePlan* plan, hipStream_t stream, void** out) {
       (void)hipFreeAsync(p, stream);
       return set_error(PA_ERR_LAUNCH, "hipMemsetAsync: %s", hipGetErrorString(e));
     }
-    if (w.ptr) (void)hipFreeAsync(w.ptr, stream);
+    if (w.ptr) {
+      if (w.captured)
+        w.retired.push_back(w.ptr);  // a graph may still replay with it
+      else
+        (void)hipFreeAsync(w.ptr, stream);
+    }
     w.ptr = p;
     w.counter_bytes = cb;
     w.part_bytes = pb;
+    w.captured = false;
   }
+  if (pa::capturing(stream)) w.captured = true;
   plan->counter_bytes = w.counter_bytes;  // partials start after the counters
   *out = w.ptr;
   return PA_OK;
@@ -331,10 +342,12 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   pp.pool = plan.pool;
   pp.max_query_len = plan.S;
   pp.causal = 0;
-  // Workgroups of 32 query rows: the S rows are few, and smaller workgroups
-  // spread them over twice as many CUs.
-  pp.row_waves = 1;
-  pp.q_tiles = (plan.S + 31) / 32;
+  // Workgroups of four waves: the S rows are few, and smaller workgroups
+  // spread them over more CUs.
+  const int hg = plan.G > 4 ? 4 : plan.G;
+  pp.row_waves = pa::kPrefixStepWaves / hg;
+  const int step_rows = pa::kPrefillWaveRows * pp.row_waves;
+  pp.q_tiles = (plan.S + step_rows - 1) / step_rows;
   pp.q = plan.q;
   pp.q_st = plan.q_ss;
   pp.q_sh = plan.q_sh;
@@ -387,7 +400,12 @@ int pa_workspace_release(void* stream_ptr) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   auto it = g_ws.find({dev, stream_ptr});
   if (it == g_ws.end()) return PA_OK;
-  const hipError_t e = hipFreeAsync(it->second.ptr, static_cast<hipStream_t>(stream_ptr));
+  const hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  hipError_t e = hipFreeAsync(it->second.ptr, stream);
+  for (void* p : it->second.retired) {
+    const hipError_t e2 = hipFreeAsync(p, stream);
+    if (e == hipSuccess) e = e2;
+  }
   g_ws.erase(it);
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "hipFreeAsync: %s", hipGetErrorString(e));
   return PA_OK;

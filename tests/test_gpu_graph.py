@@ -63,6 +63,56 @@ def test_decode_graph_replays(pa):
     pa.workspace_release(s)
 
 
+def test_decode_graph_survives_workspace_growth(pa, monkeypatch):
+    """A graph captured on a stream keeps working after a later, larger
+    eager call on that stream grows the stream's workspace: the captured
+    buffer is kept, not freed (the library frees it only at
+    pa_workspace_release).  Every replay equals the eager call bit for bit,
+    and the last one the oracle."""
+    monkeypatch.setenv("PA_DECODE_WORKERS", "256")
+    small = W.make_decode_case(811, 6, 32, 8, 128, 16, "bf16", len_range=(300, 2000))
+    big = W.make_decode_case(812, 96, 32, 8, 128, 16, "bf16", len_range=(1, 3000))
+    ds, db = case_to_dev(small), case_to_dev(big)
+    args_s = lambda: (ds["q"], ds["k_pool"], ds["v_pool"], ds["block_table"],  # noqa: E731
+                      ds["context_lens"], small.scale)
+    s = torch.cuda.Stream()
+    out_g = torch.empty(ds["q"].shape, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        pa.decode(*args_s(), out=out_g)  # sizes the stream's workspace for `small`
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pa.decode(*args_s(), out=out_g)
+    plan_s = pa.decode_plan(ds["q"], ds["k_pool"], ds["v_pool"], ds["block_table"],
+                            ds["context_lens"], out_g)
+    out_b = torch.empty(db["q"].shape, dtype=torch.float32, device="cuda")
+    plan_b = pa.decode_plan(db["q"], db["k_pool"], db["v_pool"], db["block_table"],
+                            db["context_lens"], out_b)
+    assert plan_b["workspace_bytes"] > 2 * plan_s["workspace_bytes"]  # the call below grows it
+    for i in range(3):
+        with torch.cuda.stream(s):
+            pa.decode(db["q"], db["k_pool"], db["v_pool"], db["block_table"],
+                      db["context_lens"], big.scale, out=out_b, stream=s.cuda_stream)
+        s.synchronize()
+        qi = new_q(small, 1100 + i)
+        ds["q"].copy_(to_dev(qi, small.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = pa.decode(*args_s(), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, eager), f"replay {i}"
+    ref, _ = oracle.decode(qi, small.k_pool, small.v_pool, small.block_table,
+                           small.context_lens, small.scale, small.dtype)
+    assert_close_f32_out(out_to_f64(out_g), ref, small.dtype, "last replay vs oracle")
+    ref_b, _ = oracle.decode(big.q, big.k_pool, big.v_pool, big.block_table, big.context_lens,
+                             big.scale, big.dtype)
+    assert_close_f32_out(out_to_f64(out_b), ref_b, big.dtype, "the growing call vs oracle")
+    del g
+    pa.workspace_release(s)
+    s.synchronize()
+
+
 def test_decode_capture_without_workspace_fails_cleanly(pa):
     c = W.make_decode_case(802, 8, 32, 8, 128, 16, "f16", len_range=(200, 700))
     dev = case_to_dev(c)
