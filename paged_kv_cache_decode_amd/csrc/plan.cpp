@@ -330,13 +330,16 @@ int plan_prefill(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v
   p.B = (int)B; p.MB = (int)MB; p.NB = NB;
   p.max_query_len = max_query_len;
   p.causal = causal;
-  p.q_tiles = (max_query_len + kPrefillRows - 1) / kPrefillRows;
   // Groups of 8 heads run as two workgroups of 4 heads per KV head.
   const int64_t kv_div = G > 4 ? G / 4 : 1;
+  const int hg = (int)(G / kv_div);
+  p.row_waves = kPrefillWaves / hg;
+  const int rows = kPrefillWaveRows * p.row_waves;
+  p.q_tiles = (max_query_len + rows - 1) / rows;
   p.grid[0] = (int64_t)p.q_tiles * Hkv * kv_div * S;
   p.grid[1] = 1;
   p.grid[2] = 1;
-  p.block_threads = 64 * p.row_waves * (int)(G / kv_div);  // 32 positions of one head per wave
+  p.block_threads = 64 * p.row_waves * hg;  // 16 positions of one head per wave
   p.q = q->data; p.q_st = q->stride[0]; p.q_sh = q->stride[1];
   p.k = k_pool->data; p.v = v_pool->data;
   p.pool = layout;

@@ -69,10 +69,14 @@ struct DecodePlan {
   int64_t lse_ss = 0;
 };
 
-// Query positions per prefill workgroup (all G heads of one KV head).
-constexpr int kPrefillRows = 64;
-// Waves per query head in a prefill workgroup (each wave owns 32 positions).
-constexpr int kPrefillRowWaves = kPrefillRows / 32;
+// Prefill workgroups: each wave owns 16 query positions of one head; a
+// workgroup holds min(G, 4) heads of one KV head and row_waves waves per
+// head.  Packed prompts use kPrefillWaves waves per workgroup (one workgroup
+// per compute unit, four waves per SIMD), the shared-prefix step
+// kPrefixStepWaves.
+constexpr int kPrefillWaveRows = 16;
+constexpr int kPrefillWaves = 16;
+constexpr int kPrefixStepWaves = 4;
 
 struct PrefillPlan {
   int dtype = 0, out_dtype = 0;
@@ -81,8 +85,8 @@ struct PrefillPlan {
   PoolLayout pool;
   int max_query_len = 0;
   int causal = 0;
-  int row_waves = kPrefillRowWaves;  // waves per head: 32 * row_waves query rows per workgroup
-  int q_tiles = 0;  // ceil(max_query_len / (32 * row_waves))
+  int row_waves = 0;  // waves per head: 16 * row_waves query rows per workgroup
+  int q_tiles = 0;    // ceil(max_query_len / (16 * row_waves))
   int64_t grid[3] = {0, 0, 0};
   int block_threads = 0;
   const void* q = nullptr;

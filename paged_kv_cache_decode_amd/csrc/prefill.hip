@@ -9,20 +9,23 @@
 // skipped).
 //
 // Work decomposition:
-//   workgroup = 32 * RW query positions (64 for packed prompts, 32 for the
-//   shared-prefix step) x the G query heads of one KV
-//   head (a wave owns 32 positions of one head).  K/V tiles of 64 keys
-//   are gathered once per workgroup into LDS and feed all G heads.  Key
-//   tiles wholly above the diagonal are never loaded.  LDS is double
-//   buffered: while the waves compute on one tile the next one is written
-//   to the other buffer from registers, and the tile after that is already
-//   being fetched, so there is one barrier per tile.
+//   a wave owns 16 query positions of one query head; a workgroup holds the
+//   HG heads of one KV head (HG = G, or 4 when G = 8: then two workgroups
+//   per KV head) times RW waves per head, i.e. 16 * RW positions.  Packed
+//   prompts use workgroups of 16 waves (HG * RW = 16, 64 positions x 4
+//   heads for G = 4), one per compute unit, at most 128 registers per wave:
+//   every SIMD runs four waves whose loads, matrix products and
+//   exponentials interleave.  K/V tiles of 64 keys are gathered once per
+//   workgroup into LDS and feed all its waves.  Key tiles wholly above the diagonal are never loaded.  LDS is
+//   double buffered: while the waves compute on one tile the next one is
+//   written to the other buffer from registers, and the tile after that is
+//   already being fetched, so there is one barrier per tile.
 //
-// Per 32-key half of a 64-key tile a wave computes, on 32x32x16 MFMAs:
+// Per 64-key tile a wave computes, on 16x16x32 MFMAs:
 //   S^T = K Q^T   (A = K from LDS, B = Q from registers; bf16/f16 inputs,
-//                  fp32 accumulate).  The transposed product leaves every
-//                  score of query row r in lane r (and r + 32), so the
-//                  row max / row sum of the online softmax are lane-local.
+//                  fp32 accumulate).  Every score of query row r lands in
+//                  the four lanes r, r + 16, r + 32, r + 48 (16 keys each),
+//                  so a row's max and sum take two lane swaps.
 //   O^T += V^T P^T (A = V^T from LDS, B = P from the lane's own scores,
 //                  rounded to fp16; fp32 accumulate).  V is written to LDS
 //                  transposed (d-major) and converted to fp16 while it is
@@ -50,8 +53,8 @@ namespace {
 
 constexpr int kBN = 64;                        // keys per tile
 constexpr int kD = 128;                        // head size
-constexpr int kKRow = kD * 2 + 16;             // K tile row in LDS (bytes, padded)
-constexpr int kVRow = kBN * 2 + 8;             // V^T tile row in LDS (bytes, padded)
+constexpr int kKRow = kD * 2 + 32;             // K tile row in LDS (bytes, padded)
+constexpr int kVRow = kBN * 2 + 32;            // V^T tile row in LDS (bytes, padded)
 constexpr int kKBytes = kBN * kKRow;           // one K tile in LDS
 constexpr int kVBytes = kD * kVRow;            // one V^T tile in LDS
 constexpr int kKChunks = kBN * kD * 2 / 16;    // 16-byte chunks in a K tile (1024)
@@ -97,17 +100,17 @@ struct PrefillArgs {
 };
 
 template <class T>
-__device__ __forceinline__ f32x16_t mfma_qk(u32x4_t a, u32x4_t b, f32x16_t c) {
+__device__ __forceinline__ f32x4_t mfma_qk(u32x4_t a, u32x4_t b, f32x4_t c) {
   if constexpr (__is_same(T, TBF16))
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x16_t mfma_pv(u32x4_t a, u32x4_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+__device__ __forceinline__ f32x4_t mfma_pv(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
@@ -129,33 +132,66 @@ __device__ __forceinline__ uint32_t pair_to_f16(uint32_t w0, uint32_t w1, bool h
   }
 }
 
-// The value of lane l ^ 32 (v_permlane32_swap exchanges the wave's halves
-// without going through LDS).
-__device__ __forceinline__ float swap_halves(float x) {
+// The value of lane l ^ 16 / l ^ 32.  v_permlane16_swap exchanges the odd
+// 16-lane rows of its first operand with the even rows of its second, and
+// v_permlane32_swap the wave's halves, without LDS; with both operands the
+// same register, a lane finds its partner's value in the result that its
+// own row (half) did not keep, which is picked by the lane's position.
+__device__ __forceinline__ float xor16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const bool odd = (threadIdx.x & 16) != 0;
+  return __builtin_bit_cast(float, odd ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  // r[0] holds the low half in both halves, r[1] the high half.
   const bool upper = (threadIdx.x & 32) != 0;
   return __builtin_bit_cast(float, upper ? r[0] : r[1]);
 }
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes that
+// hold one query row's scores).
+__device__ __forceinline__ float row4_max(float x) {
+  x = fmaxf(x, xor16(x));
+  return fmaxf(x, xor32(x));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  x += xor16(x);
+  return x + xor32(x);
+}
 
-// V^T rows are stored with their key-pair columns XOR-swizzled by the row's
-// 32-row group (even values, so the two dwords of a 4-key read stay
-// adjacent); it spreads the transposing writes over the LDS banks.
-__device__ __forceinline__ int vt_col(int d, int kp) { return kp ^ ((d >> 5) << 1); }
+// V^T in LDS: row d holds the tile's 64 keys as fp16, in an order that puts
+// the 8 keys one lane feeds to a P.V MFMA next to each other.  The lane
+// (row r16, group g4) of 32-key step s2 holds, as the MFMA's B operand, the
+// P values of keys 32*s2 + {4*g4 + 0..3, 16 + 4*g4 + 0..3} (the keys its
+// own S^T results cover), so within every 32 keys the key index bits
+// (4, 3..2) become (2, 4..3): the lane's 8 keys form the 16-byte chunk
+// 4*s2 + g4 of the row, read with one ds_read_b128.  The chunk index (0..7)
+// is XORed with (d >> 4) & 7 and rows are 160 bytes apart; K rows are 288
+// bytes apart.  Both strides were chosen by measuring the LDS bank-conflict
+// counter on gfx950 for these exact access patterns: the K and V^T fragment
+// reads then cost no conflict cycles and the transposing 4-byte writes of
+// the staging step two per instruction (at the 272/144-byte strides that a
+// 64-bank model predicts to be conflict-free, every fragment read cost
+// four).
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~31) | (((key >> 2) & 3) << 3) | (((key >> 4) & 1) << 2) | (key & 3);
+}
 
-// RW waves per head: a workgroup covers 32 * RW query positions.  The
-// 32-row instances (the shared-prefix step) ask for at most half the
-// register file, so that two of their workgroups can share a CU (measured:
-// prefix step 28 -> 25.5 us on the shared-prefix workload).
-template <class T, int G, int RW>
-__global__ __launch_bounds__(64 * RW * G)
-__attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(PrefillArgs a) {
-  constexpr int kNT = 64 * RW * G;  // threads
-  constexpr int kRows = 32 * RW;    // query positions per workgroup
+// HG heads x RW waves of 16 query positions per workgroup.  Sixteen-wave
+// workgroups (packed prompts) ask for at most 128 registers, four waves per
+// SIMD; four-wave ones (the shared-prefix step) for at most 256.
+template <class T, int HG, int RW>
+__global__ __launch_bounds__(64 * HG * RW)
+__attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(PrefillArgs a) {
+  constexpr int kNT = 64 * HG * RW;  // threads
+  constexpr int kRows = 16 * RW;     // query positions per workgroup
   constexpr int kKPer = kKChunks / kNT;
-  constexpr int kVPer = kVUnits / kNT;
-  static_assert(kKPer * kNT == kKChunks && kVPer * kNT == kVUnits, "tile split");
+  // With 1024 threads the first 512 stage V (one unit each); on every SIMD
+  // half of the workgroup's waves then do it.
+  constexpr int kVPer = (kVUnits + kNT - 1) / kNT;
+  constexpr bool kVAll = kVPer * kNT == kVUnits;
+  static_assert(kKPer * kNT == kKChunks && (kVAll || kVPer == 1), "tile split");
 
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][kKBytes];
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[2][kVBytes];
@@ -182,15 +218,15 @@ __attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(Prefil
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int hl = w % G;    // head within the group
-  const int half = w / G;  // which 32 of the 64 positions
-  const int hq = g * G + hl;
-  const int r32 = lane & 31;
-  const int hi = lane >> 5;
+  const int hl = w % HG;  // head within the group
+  const int rw = w / HG;  // which 16 of the workgroup's positions
+  const int hq = g * HG + hl;
+  const int r16 = lane & 15;
+  const int g4 = lane >> 4;
 
-  // This wave's rows: i = row0 + r32 (query index within the sequence).
-  const int row0 = qt * kRows + half * 32;
-  const int my_i = row0 + r32;
+  // This wave's rows: i = row0 + r16 (query index within the sequence).
+  const int row0 = qt * kRows + rw * 16;
+  const int my_i = row0 + r16;
   const bool row_ok = my_i < L;
   const int shift = n - L;  // absolute position of row i is shift + i
 
@@ -201,20 +237,21 @@ __attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(Prefil
   // Per wave: tiles below `full` need no mask; tiles from `full` up to
   // `last` need one; later tiles hold no visible key for this wave.
   const bool wave_active = row0 < L;
-  const int wave_last_i = min(row0 + 31, L - 1);
+  const int wave_last_i = min(row0 + 15, L - 1);
   const int vis_lo = a.causal ? shift + row0 : n - 1;         // first row's last key
   const int vis_hi = a.causal ? shift + wave_last_i : n - 1;  // last row's last key
   const int full = min(vis_lo + 1, n) / kBN;                  // fully visible tiles
   const int last = wave_active ? vis_hi / kBN : -1;
   const int my_vis = a.causal ? shift + my_i : n - 1;
 
-  // Q^T as the MFMA B operand: lane holds row r32, columns ks*16 + 8*hi.
-  u32x4_t qf[kD / 16];
+  // Q^T as the MFMA B operand: lane (r16, g4) holds row r16, columns
+  // 32*ks + 8*g4 .. +7.
+  u32x4_t qf[kD / 32];
   {
-    const uint8_t* qrow = a.q + (int64_t)(q0 + my_i) * a.q_st + (int64_t)hq * a.q_sh + hi * 16;
+    const uint8_t* qrow = a.q + (int64_t)(q0 + my_i) * a.q_st + (int64_t)hq * a.q_sh + g4 * 16;
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      qf[ks] = row_ok ? load16(qrow + ks * 32) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      qf[ks] = row_ok ? load16(qrow + ks * 64) : u32x4_t{0u, 0u, 0u, 0u};
       qf[ks] ^= a.q_sign;
     }
   }
@@ -251,12 +288,14 @@ __attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(Prefil
       const int kb = min(kt * kBN + 4 * wu + j * (kNT / 16), kend_c);
       kreg[j] = load16(row_addr(kbase, kb) + k_lane);
     }
+    if (kVAll || tid < kVUnits) {
 #pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int kb = min(kt * kBN + 8 * wu + j * (kNT / 8), kend_c & ~7);
-      const uint8_t* p = row_addr(vbase, kb) + v_lane;
-      vreg[j][0] = load16(p);
-      vreg[j][1] = load16(p + tok_stride);
+      for (int j = 0; j < kVPer; ++j) {
+        const int kb = min(kt * kBN + 8 * wu + j * (kNT / 8), kend_c & ~7);
+        const uint8_t* p = row_addr(vbase, kb) + v_lane;
+        vreg[j][0] = load16(p);
+        vreg[j][1] = load16(p + tok_stride);
+      }
     }
   };
   // Registers -> LDS buffer `buf` (K row-major, V transposed to fp16).  In
@@ -268,9 +307,10 @@ __attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(Prefil
     uint8_t* vl = vt_lds[buf];
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
-      const int chunk = tid + j * kNT;
-      *reinterpret_cast<u32x4_t*>(kl + (chunk >> 4) * kKRow + (chunk & 15) * 16) = kreg[j];
+      const int c = tid + j * kNT;
+      *reinterpret_cast<u32x4_t*>(kl + (c >> 4) * kKRow + (c & 15) * 16) = kreg[j];
     }
+    if (!kVAll && tid >= kVUnits) return;
     if ((kt + 1) * kBN > kend) {
 #pragma unroll
       for (int j = 0; j < kVPer; ++j) {
@@ -283,79 +323,67 @@ __attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(Prefil
 #pragma unroll
     for (int j = 0; j < kVPer; ++j) {
       const int u = tid + j * kNT;
-      const int kp = u >> 4;        // key pair
-      const int d0 = (u & 15) * 8;  // first of 8 columns
+      const int pos = vt_pos(2 * (u >> 4));  // this key pair's place in a V^T row
+      const int d0 = (u & 15) * 8;           // first of 8 columns
+      // Rows d0 .. d0+7 share the swizzle (d0 >> 4) & 7.
+      uint8_t* vp = vl + d0 * kVRow + (((pos >> 3) ^ ((d0 >> 4) & 7)) << 4) +
+                    ((pos & 7) >> 1) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int d = d0 + 2 * i;
-        *reinterpret_cast<uint32_t*>(vl + d * kVRow + vt_col(d, kp) * 4) =
+        *reinterpret_cast<uint32_t*>(vp + (2 * i) * kVRow) =
             pair_to_f16<T>(vreg[j][0][i], vreg[j][1][i], false);
-        *reinterpret_cast<uint32_t*>(vl + (d + 1) * kVRow + vt_col(d + 1, kp) * 4) =
+        *reinterpret_cast<uint32_t*>(vp + (2 * i + 1) * kVRow) =
             pair_to_f16<T>(vreg[j][0][i], vreg[j][1][i], true);
       }
     }
   };
 
-  f32x16_t acc_o[kD / 32];
+  // O^T accumulators: acc_o[db][i] is column d = 16*db + 4*g4 + i of row r16.
+  f32x4_t acc_o[kD / 16];
 #pragma unroll
-  for (int md = 0; md < kD / 32; ++md)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[md][r] = 0.f;
-  float m_run = -INFINITY;  // running max of row r32, scaled (log2 units)
+  for (int db = 0; db < kD / 16; ++db) acc_o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max of row r16, scaled (log2 units)
   float l_lane = 0.f;       // running sum of this lane's P values
 
-  // One 64-key tile of this wave as two 32-key halves, software-pipelined so
-  // that matrix-core and vector work overlap inside the wave: both halves'
-  // S^T = K Q^T MFMAs are issued first; the softmax of half 0 (VALU) then
-  // runs while half 1's QK^T executes, and the softmax of half 1 while half
-  // 0's O^T += V^T P^T executes.
   f16x2_t ones;
   ones[0] = ones[1] = static_cast<_Float16>(1.f);
-  // S^T = K Q^T for both 32-key halves of a tile.  The schedule is pinned:
-  // half 0's eight K fragments are read first, then each half-0 MFMA is
-  // followed by the read of one half-1 fragment, then half 1's MFMAs; every
-  // MFMA then finds its operand already in registers.
-  auto qk_tile = [&](const uint8_t* kl, f32x16_t& sc0, f32x16_t& sc1) {
-    const uint8_t* krow = kl + r32 * kKRow + hi * 16;
-    u32x4_t kf0[kD / 16], kf1[kD / 16];
+  // LDS fragment addresses.  K: row 16*kb + r16, bytes 64*ks + 16*g4.  V^T:
+  // row d = 16*db + r16, chunk (4*s2 + g4) ^ (db & 7) = 4*(s2 ^ (db >> 2)) +
+  // (g4 ^ (db & 3)), so a lane needs one base per value of db & 3.
+  const int k_frag = r16 * kKRow + g4 * 16;
+  int vt_frag[4];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks)
-      kf0[ks] = *reinterpret_cast<const u32x4_t*>(krow + ks * 32);
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks)
-      kf1[ks] = *reinterpret_cast<const u32x4_t*>(krow + 32 * kKRow + ks * 32);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc0[r] = sc1[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) sc0 = mfma_qk<T>(kf0[ks], qf[ks], sc0);
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) sc1 = mfma_qk<T>(kf1[ks], qf[ks], sc1);
-    __builtin_amdgcn_sched_group_barrier(0x100, kD / 16, 0);  // DS reads, half 0
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA, half 0
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read, half 1
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kD / 16, 0);  // MFMAs, half 1
-  };
-  // Online-softmax update for one half; returns P (fp16) as two MFMA B
-  // operands.  Element r of this lane is key kt*64 + mb*32 + 8*(r/4) +
-  // 4*hi + r%4.
-  auto softmax_half = [&](const f32x16_t& sc, int kt, int mb, auto mask_tag, u32x4_t* pf) {
+  for (int c = 0; c < 4; ++c) vt_frag[c] = r16 * kVRow + ((g4 ^ c) << 4);
+
+  auto compute_tile = [&](int kt, int buf, auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    bool vis[16];
-    float tmax = -INFINITY;
+    const uint8_t* kl = k_lds[buf];
+    const uint8_t* vl = vt_lds[buf];
+    // S^T = K Q^T: sc[kb][i] is the score of key kt*64 + 16*kb + 4*g4 + i.
+    f32x4_t sc[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if constexpr (kMask) {
-        const int key = kt * kBN + mb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        vis[r] = key <= my_vis;
-        tmax = fmaxf(tmax, vis[r] ? sc[r] : -INFINITY);
-      } else {
-        tmax = fmaxf(tmax, sc[r]);
+    for (int kb = 0; kb < 4; ++kb) {
+      sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks) {
+        const u32x4_t kf =
+            *reinterpret_cast<const u32x4_t*>(kl + k_frag + kb * 16 * kKRow + ks * 64);
+        sc[kb] = mfma_qk<T>(kf, qf[ks], sc[kb]);
       }
     }
-    tmax = fmaxf(tmax, swap_halves(tmax));
+    // Online-softmax update of row r16 over the tile's 64 keys.
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (kMask) {
+          const int key = kt * kBN + 16 * kb + 4 * g4 + i;
+          if (key > my_vis) sc[kb][i] = -INFINITY;
+        }
+        tmax = fmaxf(tmax, sc[kb][i]);
+      }
+    tmax = row4_max(tmax);
     // Lazy rescale: raise the running max only when some row's new max is
     // more than kRescaleSlack above it (p = 2^(s*c - m) then stays < 2^8).
     const float m_cand = tmax * a.c;
@@ -365,57 +393,33 @@ __attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(Prefil
       m_run = m_new;
       l_lane *= alpha;
 #pragma unroll
-      for (int md = 0; md < kD / 32; ++md)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[md][r] *= alpha;
+      for (int db = 0; db < kD / 16; ++db) acc_o[db] *= alpha;
     }
     const float neg_m = -m_run;
+    // P as the B operand of the two 32-key steps: step s2 holds keys
+    // 32*s2 + {4*g4 + 0..3} (sc[2*s2]) then 32*s2 + 16 + {4*g4 + 0..3}
+    // (sc[2*s2 + 1]).  Masked scores are -inf, so their P is 0.
+    u32x4_t pf[2];
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r0 = 8 * qq + 2 * j;
-        float p0 = fast_exp2(fmaf(sc[r0], a.c, neg_m));
-        float p1 = fast_exp2(fmaf(sc[r0 + 1], a.c, neg_m));
-        if constexpr (kMask) {
-          p0 = vis[r0] ? p0 : 0.f;
-          p1 = vis[r0 + 1] ? p1 : 0.f;
-        }
+        const f32x4_t& x = sc[2 * s2 + (j >> 1)];
+        const float p0 = fast_exp2(fmaf(x[2 * (j & 1)], a.c, neg_m));
+        const float p1 = fast_exp2(fmaf(x[2 * (j & 1) + 1], a.c, neg_m));
         const uint32_t pk = pack_f16(p0, p1);
-        pf[qq][j] = pk;
+        pf[s2][j] = pk;
         l_lane = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk), ones, l_lane, false);
       }
-  };
-  // O^T += V^T P^T over one half's 32 keys.
-  auto pv_half = [&](const uint8_t* vl, int mb, const u32x4_t* pf) {
-    u32x4_t vf[kD / 32][2];
+    // O^T += V^T P^T.
 #pragma unroll
-    for (int md = 0; md < kD / 32; ++md) {
-      const int d = md * 32 + r32;
-      const uint8_t* vrow = vl + d * kVRow;
+    for (int db = 0; db < kD / 16; ++db)
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        const int kp = (mb * 32 + 16 * qq + 4 * hi) >> 1;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + vt_col(d, kp) * 4);
-        const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(vrow + vt_col(d, kp + 4) * 4);
-        vf[md][qq] = u32x4_t{lo[0], lo[1], hv[0], hv[1]};
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
+            vl + vt_frag[db & 3] + db * 16 * kVRow + ((s2 ^ (db >> 2)) << 6));
+        acc_o[db] = mfma_pv(vf, pf[s2], acc_o[db]);
       }
-    }
-#pragma unroll
-    for (int md = 0; md < kD / 32; ++md)
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) acc_o[md] = mfma_pv(vf[md][qq], pf[qq], acc_o[md]);
-  };
-  auto compute_tile = [&](int kt, int buf, auto mask_tag) {
-    const uint8_t* kl = k_lds[buf];
-    const uint8_t* vl = vt_lds[buf];
-    f32x16_t sc0, sc1;
-    qk_tile(kl, sc0, sc1);
-    u32x4_t pf0[2], pf1[2];
-    softmax_half(sc0, kt, 0, mask_tag, pf0);
-    pv_half(vl, 0, pf0);
-    softmax_half(sc1, kt, 1, mask_tag, pf1);
-    pv_half(vl, 1, pf1);
   };
 
   // This workgroup's tiles: [kt0, kt1) (all of [0, ntk) without chunking).
@@ -439,78 +443,65 @@ __attribute__((amdgpu_waves_per_eu(RW == 1 ? 2 : 1))) void prefill_kernel(Prefil
     }
   }
 
-  const float l_tot = l_lane + swap_halves(l_lane);
+  const float l_tot = row4_sum(l_lane);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (a.part_o) {
     // Partial result of this key chunk: o / l and m + log2 l (log2 units of
     // the scaled scores; -inf when the chunk held no visible key), row by
-    // row ([chunk][H][rows][d]; lane (r32, hi) holds columns md*32 + 8*rg +
-    // 4*hi + 0..3 of its row).  The merge happens in the next kernel on the
+    // row ([chunk][H][rows][d]; lane (r16, g4) holds columns 16*db + 4*g4 +
+    // 0..3 of its row).  The merge happens in the next kernel on the
     // stream, after this one's writes are complete.
     if (!row_ok) return;
     const float lse = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
     const int64_t prow = ((int64_t)chunk * a.H + hq) * a.part_rows + q0 + my_i;
-    float* po = a.part_o + prow * kD;
+    float* po = a.part_o + prow * kD + 4 * g4;
 #pragma unroll
-    for (int md = 0; md < kD / 32; ++md)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg)
-        *reinterpret_cast<f32x4_t*>(po + md * 32 + 8 * rg + 4 * hi) =
-            f32x4_t{acc_o[md][4 * rg] * inv, acc_o[md][4 * rg + 1] * inv,
-                    acc_o[md][4 * rg + 2] * inv, acc_o[md][4 * rg + 3] * inv};
-    if (hi == 0) a.part_lse[prow] = lse;
+    for (int db = 0; db < kD / 16; ++db)
+      *reinterpret_cast<f32x4_t*>(po + 16 * db) = acc_o[db] * inv;
+    if (g4 == 0) a.part_lse[prow] = lse;
     return;
   }
   if (!row_ok) return;
-  const int64_t obase = (int64_t)(q0 + my_i) * a.o_st + (int64_t)hq * a.o_sh;
+  const int64_t obase = (int64_t)(q0 + my_i) * a.o_st + (int64_t)hq * a.o_sh + 4 * g4;
 #pragma unroll
-  for (int md = 0; md < kD / 32; ++md)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = md * 32 + 8 * rg + 4 * hi;
-      const float o0 = acc_o[md][4 * rg + 0] * inv, o1 = acc_o[md][4 * rg + 1] * inv;
-      const float o2 = acc_o[md][4 * rg + 2] * inv, o3 = acc_o[md][4 * rg + 3] * inv;
-      if (a.out_f32) {
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + obase + d0) =
-            f32x4_t{o0, o1, o2, o3};
+  for (int db = 0; db < kD / 16; ++db) {
+    const f32x4_t o = acc_o[db] * inv;
+    if (a.out_f32) {
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + obase + 16 * db) = o;
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(a.out) + obase + 16 * db;
+      u32x2_t pk;
+      if constexpr (__is_same(T, TBF16)) {
+        pk[0] = (uint32_t)to_bf16_bits(o[0]) | ((uint32_t)to_bf16_bits(o[1]) << 16);
+        pk[1] = (uint32_t)to_bf16_bits(o[2]) | ((uint32_t)to_bf16_bits(o[3]) << 16);
       } else {
-        uint16_t* op = static_cast<uint16_t*>(a.out) + obase + d0;
-        u32x2_t pk;
-        if constexpr (__is_same(T, TBF16)) {
-          pk[0] = (uint32_t)to_bf16_bits(o0) | ((uint32_t)to_bf16_bits(o1) << 16);
-          pk[1] = (uint32_t)to_bf16_bits(o2) | ((uint32_t)to_bf16_bits(o3) << 16);
-        } else {
-          pk[0] = (uint32_t)to_f16_bits(o0) | ((uint32_t)to_f16_bits(o1) << 16);
-          pk[1] = (uint32_t)to_f16_bits(o2) | ((uint32_t)to_f16_bits(o3) << 16);
-        }
-        *reinterpret_cast<u32x2_t*>(op) = pk;
+        pk[0] = (uint32_t)to_f16_bits(o[0]) | ((uint32_t)to_f16_bits(o[1]) << 16);
+        pk[1] = (uint32_t)to_f16_bits(o[2]) | ((uint32_t)to_f16_bits(o[3]) << 16);
       }
+      *reinterpret_cast<u32x2_t*>(op) = pk;
     }
-}
-
-template <class T, int G, int RW>
-hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t blocks = a.wg_per_xcd * 8;
-  return timed_launch("prefill", prefill_kernel<T, G, RW>, dim3((unsigned)blocks),
-                      dim3(64 * RW * G), stream, a);
-}
-
-template <class T, int RW>
-hipError_t dispatch_group(const PrefillPlan& pl, const PrefillArgs& a, hipStream_t stream) {
-  switch (pl.G) {
-    case 1: return launch_prefill_t<T, 1, RW>(a, stream);
-    case 2: return launch_prefill_t<T, 2, RW>(a, stream);
-    case 4:
-    case 8: return launch_prefill_t<T, 4, RW>(a, stream);  // 8: two workgroups per KV head
-    default: return hipErrorInvalidValue;
   }
 }
 
+template <class T, int HG, int RW>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  const int64_t blocks = a.wg_per_xcd * 8;
+  return timed_launch("prefill", prefill_kernel<T, HG, RW>, dim3((unsigned)blocks),
+                      dim3(64 * HG * RW), stream, a);
+}
+
+// Workgroups of 16 waves (packed prompts) or 4 waves (the shared-prefix
+// step): HG = min(G, 4) heads x (waves / HG) row slices.
 template <class T>
-hipError_t dispatch_rows(const PrefillPlan& pl, const PrefillArgs& a, hipStream_t stream) {
-  switch (pl.row_waves) {
-    case 1: return dispatch_group<T, 1>(pl, a, stream);
-    case 2: return dispatch_group<T, 2>(pl, a, stream);
+hipError_t dispatch_shape(const PrefillPlan& pl, const PrefillArgs& a, hipStream_t stream) {
+  const int hg = pl.G > 4 ? 4 : pl.G;
+  switch (hg * 100 + hg * pl.row_waves) {
+    case 116: return launch_prefill_t<T, 1, 16>(a, stream);
+    case 216: return launch_prefill_t<T, 2, 8>(a, stream);
+    case 416: return launch_prefill_t<T, 4, 4>(a, stream);
+    case 104: return launch_prefill_t<T, 1, 4>(a, stream);
+    case 204: return launch_prefill_t<T, 2, 2>(a, stream);
+    case 404: return launch_prefill_t<T, 4, 1>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -557,8 +548,8 @@ hipError_t launch_prefill(const PrefillPlan& pl, hipStream_t stream) {
   a.wg_per_xcd = (a.n_wg + 7) / 8;
   if (a.n_wg == 0) return hipSuccess;
   switch (pl.dtype) {
-    case PA_F16: return dispatch_rows<TF16>(pl, a, stream);
-    case PA_BF16: return dispatch_rows<TBF16>(pl, a, stream);
+    case PA_F16: return dispatch_shape<TF16>(pl, a, stream);
+    case PA_BF16: return dispatch_shape<TBF16>(pl, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
