@@ -151,6 +151,28 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_po
               const pa_tensor* out, void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, kernels and results as pa_decode
+ * (bit for bit), but the workspace is a fixed device array of 32 MiB that
+ * the library holds on each GPU it runs on until the process ends: no
+ * hipMalloc, hipFree or other allocation happens in this call.  The first
+ * call on a GPU also launches one small kernel on `stream` that zeroes the
+ * array's counter region.
+ * Limits: at most 65,536 (sequence, KV head) pairs, and at most
+ * (32 MiB - 256 KiB) of partial results, i.e. (W + S*Hkv) * G * (d + 1) * 4
+ * bytes with W the worker count (1024 on an MI355X) -- about 15,000 pairs
+ * for G = 4, d = 128.  Larger calls return PA_ERR_ALLOC with nothing
+ * launched.
+ * All calls on one GPU share the array: calls that overlap in time on one
+ * GPU (on different streams, or a graph replay next to an eager call) race
+ * and give wrong results; order them on one stream.
+ */
+int pa_decode_noalloc(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                      const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+                      const pa_tensor* out, void* stream);
+
+/*
  * pa_decode_lse -- pa_decode that also returns each (sequence, query head)'s
  * log-sum-exp of the scaled scores, lse = ln sum_t e^(scale * q . k_t)
  * (-inf for n_s = 0).  With the normalised output it is the state the

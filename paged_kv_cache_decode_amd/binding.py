@@ -48,7 +48,7 @@ class PAError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ("pa_decode", "pa_decode_shared_prefix", "pa_prefill", "pa_write_kv", "pa_copy_blocks", "pa_status_string",
+EXPORTS = ("pa_decode", "pa_decode_noalloc", "pa_decode_shared_prefix", "pa_prefill", "pa_write_kv", "pa_copy_blocks", "pa_status_string",
            "pa_last_error", "pa_decode_plan", "pa_workspace_release", "pa_profiler_enable",
            "pa_profiler_reset", "pa_profiler_read", "pa_bm_create", "pa_bm_destroy",
            "pa_bm_num_free", "pa_bm_refcount", "pa_bm_add", "pa_bm_fork", "pa_bm_append",
@@ -66,6 +66,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(PaTensor)
     L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, ctypes.c_void_p]
+    L.pa_decode_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, P, ctypes.c_void_p]
     L.pa_decode_lse.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_void_p]
     L.pa_merge_states.argtypes = [P, P, P, P, ctypes.c_void_p]
     L.pa_decode_shared_prefix.argtypes = [P, P, P, P, P, ctypes.c_int32, ctypes.c_float, P,
@@ -89,7 +90,7 @@ def lib():
     L.pa_bm_take_copies.argtypes = [V, I32P, I32P, ctypes.c_int32]
     L.pa_bm_free.argtypes = [V, ctypes.c_int64]
     L.pa_bm_block_table.argtypes = [V, I64P, ctypes.c_int32, ctypes.c_int32, I32P, I32P]
-    for f in ("pa_decode", "pa_decode_lse", "pa_merge_states", "pa_decode_shared_prefix",
+    for f in ("pa_decode", "pa_decode_noalloc", "pa_decode_lse", "pa_merge_states", "pa_decode_shared_prefix",
               "pa_prefill", "pa_write_kv",
               "pa_copy_blocks", "pa_decode_plan",
               "pa_workspace_release", "pa_profiler_enable", "pa_profiler_read", "pa_bm_num_free",
@@ -152,6 +153,20 @@ def decode(q, k_pool, v_pool, block_table, context_lens, scale, out=None, out_dt
     o = describe(out)
     _check(L.pa_decode(*[ctypes.byref(a) for a in args], ctypes.c_float(scale),
                        ctypes.byref(o), _stream(stream)))
+    return out
+
+
+def decode_noalloc(q, k_pool, v_pool, block_table, context_lens, scale, out=None,
+                   out_dtype=None, stream=None):
+    """pa_decode on the library's fixed per-GPU workspace (no allocation in
+    the call); see ``pa_decode_noalloc``."""
+    L = lib()
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    args = [describe(x) for x in (q, k_pool, v_pool, block_table, context_lens)]
+    o = describe(out)
+    _check(L.pa_decode_noalloc(*[ctypes.byref(a) for a in args], ctypes.c_float(scale),
+                               ctypes.byref(o), _stream(stream)))
     return out
 
 

@@ -281,6 +281,40 @@ int pa_decode(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_po
                      stream_ptr);
 }
 
+int pa_decode_noalloc(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
+                      const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
+                      const pa_tensor* out, void* stream_ptr) {
+  g_last_error.clear();
+  pa::DecodePlan plan;
+  int st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out, 1, &plan,
+                           &g_last_error);
+  if (st) return st;
+  if (plan.S == 0) return PA_OK;
+  st = pa::plan_decode(q, k_pool, v_pool, block_table, context_lens, scale, out,
+                       decode_workers(q, k_pool), &plan, &g_last_error);
+  if (st) return st;
+  // The fixed workspace: counters of at most kNoAllocMaxUnits units in their
+  // own region, then the partial results.
+  const int64_t units = (int64_t)plan.S * plan.Hkv;
+  const int64_t part = plan.ws_bytes - plan.counter_bytes;
+  const int64_t part_cap = pa::kNoAllocScratchBytes - pa::kNoAllocCounterBytes;
+  if (units > pa::kNoAllocMaxUnits || part > part_cap)
+    return set_error(PA_ERR_ALLOC, "pa_decode_noalloc: %lld (sequence, KV head) pairs and %lld "
+                     "bytes of partial results exceed its fixed workspace (at most %lld pairs "
+                     "and %lld bytes); use pa_decode", (long long)units, (long long)part,
+                     (long long)pa::kNoAllocMaxUnits, (long long)part_cap);
+  plan.counter_bytes = pa::kNoAllocCounterBytes;
+  plan.ws_bytes = plan.counter_bytes + part;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  void* ws = nullptr;
+  hipError_t e = pa::noalloc_workspace(stream, &ws);
+  if (e != hipSuccess)
+    return set_error(PA_ERR_LAUNCH, "pa_decode_noalloc workspace: %s", hipGetErrorString(e));
+  e = pa::launch_decode(plan, ws, stream);
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 int pa_decode_lse(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor* v_pool,
                   const pa_tensor* block_table, const pa_tensor* context_lens, float scale,
                   const pa_tensor* out, const pa_tensor* lse, void* stream_ptr) {

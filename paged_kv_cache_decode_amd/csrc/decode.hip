@@ -858,6 +858,49 @@ int decode_worker_count(int dtype, int D, int G) {
   return w;
 }
 
+namespace {
+
+// pa_decode_noalloc's workspace: a file-scope device array, one copy per GPU
+// that the library runs on, held until the process ends.  In host code its
+// name is only a stand-in; the device address of the current GPU's copy
+// comes from hipGetSymbolAddress (noalloc_workspace) and is what kernels
+// and copies get.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t noalloc_workspace(hipStream_t stream, void** ws) {
+  static std::mutex mu;
+  static std::map<int, void*> per_device;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = per_device.find(dev);
+  if (it != per_device.end()) {
+    *ws = it->second;
+    return hipSuccess;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  // Set-up on this GPU: the counter region starts at zero (a kernel, not a
+  // memset, so that a first call inside a graph capture records no memset
+  // node).  Every later call leaves the counters it uses at zero again.
+  hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(ptr), kNoAllocCounterBytes / 4);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  per_device[dev] = ptr;
+  *ws = ptr;
+  return hipSuccess;
+}
+
 hipError_t launch_decode(const DecodePlan& pl, void* workspace, hipStream_t stream) {
   DecodeArgs a;
   const int e = pl.dtype == PA_F32 ? 4 : 2;

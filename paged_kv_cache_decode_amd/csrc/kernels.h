@@ -12,6 +12,11 @@ namespace pa {
 // holds plan.ws_bytes bytes.
 hipError_t launch_decode(const DecodePlan& plan, void* workspace, hipStream_t stream);
 
+// This GPU's copy of pa_decode_noalloc's fixed workspace (decode.hip): its
+// device address, looked up once per device, whose counter region is zeroed
+// on `stream` at that first call.
+hipError_t noalloc_workspace(hipStream_t stream, void** ws);
+
 // Decode workers for this instance on the current device: one workgroup of
 // kDecodeWaves wavefronts per compute unit (an MI355X's 256 CUs without a
 // device).

@@ -69,6 +69,16 @@ struct DecodePlan {
   int64_t lse_ss = 0;
 };
 
+// pa_decode_noalloc runs on a fixed device array of kNoAllocScratchBytes per
+// GPU instead of an allocated workspace.  Its first kNoAllocCounterBytes
+// hold the per-unit counters of at most kNoAllocMaxUnits (sequence, KV head)
+// pairs -- a region that never holds anything else, so the counters, which
+// the kernel leaves at zero, stay zero between calls of any size -- and the
+// partial results follow.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)32 << 20;
+constexpr int64_t kNoAllocMaxUnits = (int64_t)1 << 16;
+constexpr int64_t kNoAllocCounterBytes = kNoAllocMaxUnits * 4;
+
 // Prefill workgroups: each wave owns 16 query positions of one head; a
 // workgroup holds min(G, 4) heads of one KV head and row_waves waves per
 // head.  Packed prompts use kPrefillWaves waves per workgroup (one workgroup

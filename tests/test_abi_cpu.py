@@ -256,3 +256,23 @@ def test_decode_lse_and_merge_reject():
     for po_, pl_, out_, status in cases:
         st = L.pa_merge_states(r(po_), r(pl_), r(out_), None, None)
         assert st == status, L.pa_last_error()
+
+
+def test_decode_noalloc_rejects_what_its_fixed_workspace_cannot_hold(monkeypatch):
+    """pa_decode_noalloc validates like pa_decode, then refuses calls whose
+    counters or partial results exceed its fixed per-GPU array -- before any
+    device work (fake pointers here)."""
+    L = B.lib()
+    r = ctypes.byref
+
+    def call(a):
+        return L.pa_decode_noalloc(r(a["q"]), r(a["k"]), r(a["v"]), r(a["bt"]), r(a["cl"]),
+                                   ctypes.c_float(0.1), r(a["out"]), None)
+
+    a = decode_args()
+    a["bt"].dtype = B.PA_F32
+    assert call(a) == -2  # the same validation as pa_decode
+    assert call(decode_args(S=9000, H=8, Hkv=8)) == -6  # 72,000 (sequence, KV head) pairs
+    assert "fixed workspace" in L.pa_last_error().decode()
+    monkeypatch.setenv("PA_DECODE_WORKERS", "100000")  # 100,032 partial slots of 2,064 bytes
+    assert call(decode_args()) == -6
