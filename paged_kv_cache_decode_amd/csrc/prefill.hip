@@ -279,62 +279,43 @@ __attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(
     return base + phys * block_bytes + (int64_t)((key & bmask) * tok_stride);
   };
 
-  // Global -> registers for tile kt.
-  u32x4_t kreg[kKPer];
-  u32x4_t vreg[kVPer][2];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int kb = min(kt * kBN + 4 * wu + j * (kNT / 16), kend_c);
-      kreg[j] = load16(row_addr(kbase, kb) + k_lane);
-    }
-    if (kVAll || tid < kVUnits) {
-#pragma unroll
-      for (int j = 0; j < kVPer; ++j) {
-        const int kb = min(kt * kBN + 8 * wu + j * (kNT / 8), kend_c & ~7);
-        const uint8_t* p = row_addr(vbase, kb) + v_lane;
-        vreg[j][0] = load16(p);
-        vreg[j][1] = load16(p + tok_stride);
-      }
-    }
+  // Staging pieces.  K: one 16-byte chunk of key row kb + (lane >> 4) (four
+  // keys per load instruction), stored as chunk c of the row-major tile.  V:
+  // the same 16 bytes (8 columns) of two consecutive key rows, stored
+  // transposed to fp16 (unit u: key pair u >> 4, columns (u & 15) * 8 ..).
+  auto k_load = [&](int kt, int key_off) -> u32x4_t {
+    const int kb = min(kt * kBN + key_off, kend_c);
+    return load16(row_addr(kbase, kb) + k_lane);
   };
-  // Registers -> LDS buffer `buf` (K row-major, V transposed to fp16).  In
-  // the tile that reaches `kend`, V rows at or past it are zeroed first (they
-  // may be clamped duplicates or unwritten slots; P is zero there, and a
-  // zero row keeps the product finite).
-  auto store_tile = [&](int kt, int buf) {
-    uint8_t* kl = k_lds[buf];
-    uint8_t* vl = vt_lds[buf];
-#pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int c = tid + j * kNT;
-      *reinterpret_cast<u32x4_t*>(kl + (c >> 4) * kKRow + (c & 15) * 16) = kreg[j];
-    }
-    if (!kVAll && tid >= kVUnits) return;
+  auto k_store = [&](uint8_t* kl, int c, u32x4_t x) {
+    *reinterpret_cast<u32x4_t*>(kl + (c >> 4) * kKRow + (c & 15) * 16) = x;
+  };
+  auto v_load = [&](int kt, int key_off, u32x4_t (&vr)[2]) {
+    const int kb = min(kt * kBN + key_off, kend_c & ~7);
+    const uint8_t* p = row_addr(vbase, kb) + v_lane;
+    vr[0] = load16(p);
+    vr[1] = load16(p + tok_stride);
+  };
+  // In the tile that reaches `kend`, V rows at or past it are zeroed first
+  // (they may be clamped duplicates or unwritten slots; P is zero there, and
+  // a zero row keeps the product finite).
+  auto v_store = [&](int kt, uint8_t* vl, int u, u32x4_t (&vr)[2]) {
     if ((kt + 1) * kBN > kend) {
+      const int key = kt * kBN + 2 * (u >> 4);
 #pragma unroll
-      for (int j = 0; j < kVPer; ++j) {
-        const int key = kt * kBN + 2 * ((tid + j * kNT) >> 4);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          if (key + t >= kend) vreg[j][t] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      for (int t = 0; t < 2; ++t)
+        if (key + t >= kend) vr[t] = u32x4_t{0u, 0u, 0u, 0u};
     }
+    const int pos = vt_pos(2 * (u >> 4));  // this key pair's place in a V^T row
+    const int d0 = (u & 15) * 8;           // first of 8 columns
+    // Rows d0 .. d0+7 share the swizzle (d0 >> 4) & 7.
+    uint8_t* vp = vl + d0 * kVRow + (((pos >> 3) ^ ((d0 >> 4) & 7)) << 4) +
+                  ((pos & 7) >> 1) * 4;
 #pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int u = tid + j * kNT;
-      const int pos = vt_pos(2 * (u >> 4));  // this key pair's place in a V^T row
-      const int d0 = (u & 15) * 8;           // first of 8 columns
-      // Rows d0 .. d0+7 share the swizzle (d0 >> 4) & 7.
-      uint8_t* vp = vl + d0 * kVRow + (((pos >> 3) ^ ((d0 >> 4) & 7)) << 4) +
-                    ((pos & 7) >> 1) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint32_t*>(vp + (2 * i) * kVRow) =
-            pair_to_f16<T>(vreg[j][0][i], vreg[j][1][i], false);
-        *reinterpret_cast<uint32_t*>(vp + (2 * i + 1) * kVRow) =
-            pair_to_f16<T>(vreg[j][0][i], vreg[j][1][i], true);
-      }
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint32_t*>(vp + (2 * i) * kVRow) = pair_to_f16<T>(vr[0][i], vr[1][i], false);
+      *reinterpret_cast<uint32_t*>(vp + (2 * i + 1) * kVRow) =
+          pair_to_f16<T>(vr[0][i], vr[1][i], true);
     }
   };
 
@@ -344,6 +325,8 @@ __attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(
   for (int db = 0; db < kD / 16; ++db) acc_o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;  // running max of row r16, scaled (log2 units)
   float l_lane = 0.f;       // running sum of this lane's P values
+  f32x4_t sc[4];            // S^T of the current tile: key kt*64 + 16*kb + 4*g4 + i
+  u32x4_t pf[2];            // its P, as the B operands of the two 32-key steps
 
   f16x2_t ones;
   ones[0] = ones[1] = static_cast<_Float16>(1.f);
@@ -355,12 +338,9 @@ __attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c) vt_frag[c] = r16 * kVRow + ((g4 ^ c) << 4);
 
-  auto compute_tile = [&](int kt, int buf, auto mask_tag) {
-    constexpr bool kMask = decltype(mask_tag)::value;
-    const uint8_t* kl = k_lds[buf];
-    const uint8_t* vl = vt_lds[buf];
-    // S^T = K Q^T: sc[kb][i] is the score of key kt*64 + 16*kb + 4*g4 + i.
-    f32x4_t sc[4];
+  // S^T = K Q^T for tile kt (K in buffer kt & 1).
+  auto qk_step = [&](int kt) {
+    const uint8_t* kl = k_lds[kt & 1];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -371,7 +351,10 @@ __attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(
         sc[kb] = mfma_qk<T>(kf, qf[ks], sc[kb]);
       }
     }
-    // Online-softmax update of row r16 over the tile's 64 keys.
+  };
+  // Online-softmax update of row r16 over tile kt's 64 keys: sc -> pf.
+  auto softmax_step = [&](int kt, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -399,7 +382,6 @@ __attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(
     // P as the B operand of the two 32-key steps: step s2 holds keys
     // 32*s2 + {4*g4 + 0..3} (sc[2*s2]) then 32*s2 + 16 + {4*g4 + 0..3}
     // (sc[2*s2 + 1]).  Masked scores are -inf, so their P is 0.
-    u32x4_t pf[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -411,7 +393,16 @@ __attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(
         pf[s2][j] = pk;
         l_lane = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk), ones, l_lane, false);
       }
-    // O^T += V^T P^T.
+  };
+  auto softmax_tile = [&](int kt) {
+    if (kt < full)
+      softmax_step(kt, std::false_type{});
+    else
+      softmax_step(kt, std::true_type{});
+  };
+  // O^T += V^T P^T for tile kt (V^T in buffer kt & 1).
+  auto pv_step = [&](int kt) {
+    const uint8_t* vl = vt_lds[kt & 1];
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db)
 #pragma unroll
@@ -425,21 +416,41 @@ __attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(
   // This workgroup's tiles: [kt0, kt1) (all of [0, ntk) without chunking).
   const int kt0 = min(ntk, chunk * a.chunk_tiles);
   const int kt1 = min(ntk, kt0 + a.chunk_tiles);
+  // One phase per tile for all waves: while they compute on tile kt, tile
+  // kt + 1 is written to the other buffers and tile kt + 2 is fetched.
+  u32x4_t kreg[kKPer];
+  u32x4_t vreg[kVPer][2];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) kreg[j] = k_load(kt, 4 * wu + j * (kNT / 16));
+    if (kVAll || tid < kVUnits) {
+#pragma unroll
+      for (int j = 0; j < kVPer; ++j) v_load(kt, 8 * wu + j * (kNT / 8), vreg[j]);
+    }
+  };
+  auto store_tile = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) k_store(k_lds[kt & 1], tid + j * kNT, kreg[j]);
+    if (kVAll || tid < kVUnits) {
+#pragma unroll
+      for (int j = 0; j < kVPer; ++j) v_store(kt, vt_lds[kt & 1], tid + j * kNT, vreg[j]);
+    }
+  };
   if (kt0 < kt1) {
     load_tile(kt0);
-    store_tile(kt0, kt0 & 1);
+    store_tile(kt0);
     if (kt0 + 1 < kt1) load_tile(kt0 + 1);
   }
   for (int kt = kt0; kt < kt1; ++kt) {
     __syncthreads();  // tile kt is in buffer kt & 1; buffer (kt+1) & 1 is free
     if (kt + 1 < kt1) {
-      store_tile(kt + 1, (kt + 1) & 1);
+      store_tile(kt + 1);
       if (kt + 2 < kt1) load_tile(kt + 2);
     }
-    if (kt < full) {
-      compute_tile(kt, kt & 1, std::false_type{});
-    } else if (kt <= last) {
-      compute_tile(kt, kt & 1, std::true_type{});
+    if (kt <= last) {
+      qk_step(kt);
+      softmax_tile(kt);
+      pv_step(kt);
     }
   }
 
