@@ -18,12 +18,17 @@ The same line carries:
   launch stream, over a second pass of the same K steps; ``traffic`` comes
   from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when that
   summary was taken on the current kernel source, else null.
-* ``cpu_baseline``: the fp64 CPU oracle on the same workload.
+* ``step_us`` / ``kernel_us``: median, p10 and p90 of the per-step times
+  (HIP events between steps, a pass of their own) and of the per-launch
+  kernel times.
+* ``cpu_baseline``: the fp64 CPU oracle on the same workload, with the
+  host's CPU count, affinity set and BLAS threads.
 * ``extra``: the long-context decode (4 x 100,000 keys, bf16), the GQA and
   long-context decodes again with pools head-major within blocks (the other
   pool layout the library reads), the prefix-shared decode sweep
   (B = 16/32/64/128), the causal prefill (8 prompts of 512..4096 tokens,
-  bf16; TFLOP/s against the bf16 MFMA peak) and, as context for the HBM
+  bf16; TFLOP/s against the bf16 MFMA peak, and against the peak at the
+  shader clock measured while it runs) and, as context for the HBM
   fractions, the rate of a plain 1 GiB device copy.
 """
 
@@ -32,7 +37,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -62,6 +66,12 @@ def parse():
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of a "
                          "workload run and of a --copy-calibration run into "
                          "profiles/<KERNEL>_<WORKLOAD>_traffic.json (no GPU needed)")
+    ap.add_argument("--rdreq-check", nargs=4, default=None,
+                    metavar=("KERNEL", "WORKLOAD", "RDREQ_CSV", "COPY_RDREQ_CSV"),
+                    help="add to profiles/<KERNEL>_<WORKLOAD>_traffic.json the read bytes "
+                         "given by the TCC_EA0_RDREQ_{32B,64B,128B} request counts of a "
+                         "workload run and of a --copy-calibration run: an independent "
+                         "check of the FETCH_SIZE scale factor (no GPU needed)")
     ap.add_argument("--only", default="",
                     help="comma list of workloads to run (for profiling): "
                          "gqa,long,gqa-hm,long-hm,share,prefix,prefill,copy; prefix16 runs "
@@ -101,8 +111,8 @@ def load_traffic(kernel, workload, src_hash, bytes_per_launch):
 
 # Kernel record name -> (substring of its demangled symbol, source).  The
 # last three tell apart the kernels of the prefix-shared workload: plain
-# decode, and the shared-prefix call's prefix step (32-row prefill) and
-# suffix step (whole-row K).
+# decode, and the shared-prefix call's prefix step (the prefill kernel with
+# one 16-row wave per head) and suffix step (whole-row K).
 KERNEL_SOURCES = {"decode_partitions": ("decode_partitions_kernel", "decode.hip"),
                   "prefill": ("prefill_kernel", "prefill.hip"),
                   "decode_partitions_plain":
@@ -113,9 +123,10 @@ KERNEL_SOURCES = {"decode_partitions": ("decode_partitions_kernel", "decode.hip"
 COPY_CALIBRATION_BYTES = 1 << 30
 
 
-def counter_mean_kib(path, name_part, counter):
-    """Mean per-dispatch value (KiB) of `counter` over dispatches whose kernel
-    symbol contains `name_part`, from a rocprofv3 counter_collection.csv."""
+def counter_mean(path, name_part, counter):
+    """Mean per-dispatch value of `counter` over dispatches whose kernel
+    symbol contains `name_part`, from a rocprofv3 counter_collection.csv
+    (FETCH_SIZE / WRITE_SIZE are in KiB, request counters are counts)."""
     import csv
     vals = []
     with open(path, newline="") as f:
@@ -131,12 +142,12 @@ def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_w
     """FETCH_SIZE / WRITE_SIZE per launch, each scaled by what the same
     counter reports for a plain device copy of known size."""
     part, src_file = KERNEL_SOURCES[kernel]
-    cf, _ = counter_mean_kib(copy_fetch_csv, "copyBuffer", "FETCH_SIZE")
-    cw, _ = counter_mean_kib(copy_write_csv, "copyBuffer", "WRITE_SIZE")
+    cf, _ = counter_mean(copy_fetch_csv, "copyBuffer", "FETCH_SIZE")
+    cw, _ = counter_mean(copy_write_csv, "copyBuffer", "WRITE_SIZE")
     fetch_scale = COPY_CALIBRATION_BYTES / (cf * 1024.0)
     write_scale = COPY_CALIBRATION_BYTES / (cw * 1024.0)
-    fk, nf = counter_mean_kib(fetch_csv, part, "FETCH_SIZE")
-    wk, nw = counter_mean_kib(write_csv, part, "WRITE_SIZE")
+    fk, nf = counter_mean(fetch_csv, part, "FETCH_SIZE")
+    wk, nw = counter_mean(write_csv, part, "WRITE_SIZE")
     rec = {"kernel": kernel, "workload": workload, "source_hash": source_hash(src_file),
            "fetch_bytes": round(fk * 1024.0 * fetch_scale),
            "write_bytes": round(wk * 1024.0 * write_scale),
@@ -150,6 +161,38 @@ def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_w
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+
+
+def rdreq_bytes(path, name_part):
+    """Mean per-dispatch read bytes from the memory-request counts of the
+    dispatches whose kernel symbol contains `name_part`: 32, 64 and 128 B
+    requests counted separately, plus their total as a consistency check."""
+    sizes = {"TCC_EA0_RDREQ_32B": 32, "TCC_EA0_RDREQ_64B": 64, "TCC_EA0_RDREQ_128B": 128}
+    got = {}
+    for c in (*sizes, "TCC_EA0_RDREQ"):
+        got[c], _ = counter_mean(path, name_part, c)
+    nbytes = sum(got[c] * b for c, b in sizes.items())
+    return nbytes, got
+
+
+def rdreq_check(kernel, workload, rdreq_csv, copy_rdreq_csv):
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    with open(path) as f:
+        rec = json.load(f)
+    part, _ = KERNEL_SOURCES[kernel]
+    kb, kc = rdreq_bytes(rdreq_csv, part)
+    cb, cc = rdreq_bytes(copy_rdreq_csv, "copyBuffer")
+    rec["rdreq_cross_check"] = {
+        "read_bytes_from_request_counts": round(kb),
+        "over_scaled_fetch_bytes": round(kb / rec["fetch_bytes"], 4),
+        "over_raw_fetch_size": round(kb / (rec["fetch_kib_raw"] * 1024.0), 4),
+        "copy_read_bytes_over_1GiB": round(cb / COPY_CALIBRATION_BYTES, 4),
+        "request_counts": {k: round(v) for k, v in kc.items()},
+        "copy_request_counts": {k: round(v) for k, v in cc.items()}}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec["rdreq_cross_check"]))
 
 
 def prefix_dram_measured(unique):
@@ -192,10 +235,83 @@ class Timer:
         self.torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
+    def step_times_ms(self, fn, steps):
+        """Per-step durations from HIP events recorded between the steps on
+        the stream the library launches on (a pass of its own, so the
+        event packets stay out of the wall-clock pass)."""
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            ev[i].record()
+            fn(i)
+        ev[steps].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def spread_us(ms):
+    """Median, p10 and p90 of a list of millisecond timings, in us."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    if a.size == 0:
+        return None
+    p10, p50, p90 = np.percentile(a, [10, 50, 90])
+    return {"median": round(float(p50), 2), "p10": round(float(p10), 2),
+            "p90": round(float(p90), 2), "n": int(a.size)}
+
+
+def shader_mhz_during(torch, binding, fn, steps, est_step_sec):
+    """Shader clock (MHz) while `steps` steps run: pa_clock_probe's single
+    wave on a side stream (default priority) counts shader-clock ticks over
+    about 80 % of the steps' expected span of 100 MHz reference ticks.  A
+    pass of its own, so the probe's wave slot stays out of the timed
+    passes."""
+    side = torch.cuda.Stream()
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    ticks = int(min(1e8, max(1e4, 0.8 * est_step_sec * steps * 1e8)))
+    torch.cuda.synchronize()
+    binding.clock_probe(out, ticks, stream=side)
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    c, r = (int(x) for x in out.tolist())
+    mhz = 100.0 * c / r if r > 0 else float("nan")
+    return mhz if 300.0 < mhz < 4000.0 else None
+
+
+def host_info():
+    """What the CPU baseline could use on this host."""
+    import numpy  # noqa: F401  (loads the BLAS threadpoolctl reports)
+    info = {"os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas"] = [{"library": p.get("internal_api"), "threads": p.get("num_threads")}
+                        for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception as e:  # threadpoolctl missing or failing: say so
+        info["blas"] = f"unavailable: {e}"
+    return info
+
+
+def blas_threads(info):
+    blas = info.get("blas")
+    if isinstance(blas, list) and blas:
+        return max(int(b["threads"] or 1) for b in blas)
+    return 1
+
+
+def workload_meta(case):
+    return {"seed": case.meta["seed"], "NB": int(case.meta["NB"]), "MB": int(case.meta["MB"])}
+
 
 def kernel_avg_ms(binding, name):
     ms, n = binding.profiler_read(name)
     return (ms / n if n else float("nan")), n
+
+
+def kernel_spread(binding, name):
+    return spread_us(binding.profiler_samples(name))
 
 
 def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
@@ -222,13 +338,17 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
     binding.profiler_enable(False)
     part_ms, part_n = kernel_avg_ms(binding, "decode_partitions")
     pre_ms, pre_n = kernel_avg_ms(binding, "prefill")
+    part_spread = kernel_spread(binding, "decode_partitions")
+    pre_spread = kernel_spread(binding, "prefill") if pre_n else None
     binding.profiler_reset()
+    step_spread = spread_us(timer.step_times_ms(step, steps))
     del calls, devs
     torch.cuda.synchronize()
     binding.workspace_release()
     torch.cuda.empty_cache()
     return dict(sec=sec, part_ms=part_ms, part_launches=part_n, plan=plan,
-                prefix_ms=pre_ms if pre_n else 0.0)
+                prefix_ms=pre_ms if pre_n else 0.0, part_spread=part_spread,
+                prefix_spread=pre_spread, step_spread=step_spread)
 
 
 def bench_long_share(torch, binding, W, steps):
@@ -310,13 +430,16 @@ def cpu_oracle_decode(case, budget_s=10.0, max_passes=8):
             break
     wall = time.perf_counter() - t0
     cpu = time.process_time() - c0
-    return wall / passes, max(1, math.ceil(cpu / wall)), passes
+    return wall / passes, cpu / wall, passes
 
 
 def main():
     a = parse()
     if a.write_traffic:
         write_traffic(*a.write_traffic)
+        return
+    if a.rdreq_check:
+        rdreq_check(*a.rdreq_check)
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the decode and "
@@ -359,6 +482,7 @@ def main():
                 "traffic": load_traffic("decode_partitions", "gqa-f16-decode", src, nbytes),
                 "kernel": "decode_partitions_kernel<f16,128,4>",
                 "kernel_avg_us": round(r["part_ms"] * 1e3, 2),
+                "kernel_us": r["part_spread"],
                 "algorithmic_bytes_per_launch": nbytes}
         result = {
             "metric": "Paged attn: decode HBM GB/s (% of peak); causal prefill TFLOP/s "
@@ -369,6 +493,7 @@ def main():
             "steps": a.steps,
             "warmup": a.warmup,
             "ms_per_step": round(r["sec"] * 1e3, 4),
+            "step_us": r["step_spread"],
             "higher_is_better": True,
             "scaling": "weak",
             "vs_baseline": None,
@@ -377,17 +502,21 @@ def main():
             "config": {"workload": "gqa-f16-decode", "seqs": 64, "heads": 32, "kv_heads": 8,
                        "head_dim": 128, "block_size": 16, "context": "uniform[128,4096]",
                        "total_keys": int(case.context_lens.sum()), "out": "f16",
-                       "pool_copies_rotated": 3, "decode_workers": r["plan"]["workers"]},
+                       "pool_copies_rotated": 3, "decode_workers": r["plan"]["workers"],
+                       **workload_meta(case)},
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "roofline": roof,
         }
         if not a.headline_only and not a.no_cpu_baseline:
-            sec, cores, passes = cpu_oracle_decode(case)
+            sec, busy, passes = cpu_oracle_decode(case)
+            host = host_info()
             result["cpu_baseline"] = {
-                "value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
+                "value": round(nbytes / sec / 1e9, 4), "unit": "GB/s",
+                "cores": min(blas_threads(host), host["affinity_cpus"]),
                 "kind": "oracle",
                 "sample": f"the whole workload (64 sequences x 32 heads), {passes} pass(es), "
-                          f"{sec:.2f} s per pass, fp64 numpy"}
+                          f"{sec:.2f} s per pass, fp64 numpy",
+                "host": host, "avg_busy_threads": round(busy, 2)}
         del case
 
     if not a.headline_only:
@@ -397,13 +526,24 @@ def main():
             nbytes = W.decode_bytes(case, out_bytes_per_elem=2)
             r = bench_decode_case(torch, binding, case, max(10, a.steps // 2), 3, 1,
                                   torch.bfloat16)
+            lgbs = nbytes / (r["part_ms"] * 1e-3) / 1e9
             extra["long-bf16-decode"] = {
                 "GB/s": round(nbytes / r["sec"] / 1e9, 1),
                 "frac_of_hbm_peak": round(nbytes / r["sec"] / 1e9 / HBM_PEAK_GBS, 4),
                 "ms_per_step": round(r["sec"] * 1e3, 4),
-                "partition_kernel_GB/s": round(nbytes / (r["part_ms"] * 1e-3) / 1e9, 1),
-                "partition_kernel_avg_us": round(r["part_ms"] * 1e3, 2),
+                "step_us": r["step_spread"],
+                "roofline": {"bound": "hbm", "achieved": round(lgbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(lgbs / HBM_PEAK_GBS, 4),
+                             "traffic": load_traffic("decode_partitions", "long-bf16-decode",
+                                                     source_hash("decode.hip"), nbytes),
+                             "kernel": "decode_partitions_kernel<bf16,128,4>",
+                             "kernel_avg_us": round(r["part_ms"] * 1e3, 2),
+                             "kernel_us": r["part_spread"],
+                             "algorithmic_bytes_per_launch": nbytes},
                 "decode_workers": r["plan"]["workers"],
+                "config": {"seqs": 4, "heads": 32, "kv_heads": 8, "head_dim": 128,
+                           "block_size": 16, "context": 100_000, "out": "bf16",
+                           **workload_meta(case)},
                 "algorithmic_bytes": nbytes}
             del case
         # ---- the same two workloads with head-major blocks (layout option) ----
@@ -424,7 +564,10 @@ def main():
                 "ms_per_step": round(rh["sec"] * 1e3, 4),
                 "partition_kernel_GB/s": round(nbytes / (rh["part_ms"] * 1e-3) / 1e9, 1),
                 "partition_kernel_avg_us": round(rh["part_ms"] * 1e3, 2),
-                "pool_layout": "[NB, Hkv, B, d] memory, viewed as [NB, B, Hkv, d]"}
+                "partition_kernel_us": rh["part_spread"],
+                "step_us": rh["step_spread"],
+                "pool_layout": "[NB, Hkv, B, d] memory, viewed as [NB, B, Hkv, d]",
+                "config": workload_meta(case)}
             del case
         # ---- one GPU's share of the long context split eight ways ----------
         if want("share"):
@@ -446,15 +589,21 @@ def main():
                     "frac_of_hbm_peak_unique": round(unique / r["sec"] / 1e9 / HBM_PEAK_GBS, 4),
                     "logical_GB/s": round(logical / r["sec"] / 1e9, 1),
                     "ms_per_step": round(r["sec"] * 1e3, 4),
+                    "step_us": r["step_spread"],
                     "partition_kernel_avg_us": round(r["part_ms"] * 1e3, 2),
+                    "partition_kernel_us": r["part_spread"],
                     "shared_prefix_call": {
                         "unique_GB/s": round(unique / rc["sec"] / 1e9, 1),
                         "frac_of_hbm_peak_unique": round(unique / rc["sec"] / 1e9 /
                                                          HBM_PEAK_GBS, 4),
                         "ms_per_step": round(rc["sec"] * 1e3, 4),
+                        "step_us": rc["step_spread"],
                         "prefix_kernel_avg_us": round(rc["prefix_ms"] * 1e3, 2),
-                        "suffix_kernel_avg_us": round(rc["part_ms"] * 1e3, 2)},
-                    "unique_bytes": unique, "logical_bytes": logical}
+                        "prefix_kernel_us": rc["prefix_spread"],
+                        "suffix_kernel_avg_us": round(rc["part_ms"] * 1e3, 2),
+                        "suffix_kernel_us": rc["part_spread"]},
+                    "unique_bytes": unique, "logical_bytes": logical,
+                    "config": {**workload_meta(case), "prefix_len": case.meta["prefix_len"]}}
                 if B == 16:
                     extra["prefix-shared-bf16-decode-B16"]["dram_measured"] = \
                         prefix_dram_measured(unique)
@@ -478,21 +627,35 @@ def main():
             timer.run(lambda i: call(), steps)
             binding.profiler_enable(False)
             k_ms, _ = kernel_avg_ms(binding, "prefill")
+            k_spread = kernel_spread(binding, "prefill")
             binding.profiler_reset()
+            step_spread = spread_us(timer.step_times_ms(lambda i: call(), steps))
+            mhz = shader_mhz_during(torch, binding, lambda i: call(), steps, sec)
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
             tf = flops / sec / 1e12
             ktf = flops / (k_ms * 1e-3) / 1e12
-            entry = {"TFLOP/s": round(tf, 1), "frac_of_bf16_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4),
-                     "ms_per_step": round(sec * 1e3, 4), "flops": flops,
-                     "prompt_lens": case.meta["lens"],
-                     "roofline": {"bound": "mfma", "achieved": round(ktf, 1),
-                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": round(ktf / BF16_PEAK_TFLOPS, 4),
-                                  "kernel": "prefill_kernel<bf16,4>",
-                                  "kernel_avg_us": round(k_ms * 1e3, 2),
-                                  "traffic": load_traffic(
-                                      "prefill", "causal-bf16-prefill",
-                                      source_hash("prefill.hip"),
-                                      W.prefill_bytes(case))}}
+            roof = {"bound": "mfma", "achieved": round(ktf, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ktf / BF16_PEAK_TFLOPS, 4),
+                    "kernel": "prefill_kernel<bf16,4,4>",
+                    "kernel_avg_us": round(k_ms * 1e3, 2), "kernel_us": k_spread,
+                    "traffic": load_traffic("prefill", "causal-bf16-prefill",
+                                            source_hash("prefill.hip"),
+                                            W.prefill_bytes(case))}
+            if mhz:
+                # 4096 dense bf16 FLOPs per clock per CU (2.5 PFLOP/s nominal
+                # is 256 CUs x 2.4 GHz x 4096).
+                measured_peak = cus * mhz * 1e6 * 4096 / 1e12
+                roof["clock_measured"] = {
+                    "shader_MHz": round(mhz, 1), "compute_units": cus,
+                    "peak_at_measured_clock": round(measured_peak, 1),
+                    "frac_at_measured_clock": round(ktf / measured_peak, 4),
+                    "how": "pa_clock_probe wave on a side stream during a separate pass "
+                           "of the same steps"}
+            entry = {"TFLOP/s": round(tf, 1),
+                     "frac_of_bf16_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                     "ms_per_step": round(sec * 1e3, 4), "step_us": step_spread,
+                     "flops": flops, "prompt_lens": case.meta["lens"],
+                     "config": workload_meta(case), "roofline": roof}
             if not a.no_cpu_baseline:
                 import oracle
                 # The prompts one by one, all 32 heads, until all are done or
@@ -515,9 +678,11 @@ def main():
                 cpu = time.process_time() - c0
                 what = ("the whole workload" if len(done) == case.num_seqs else
                         f"the first {len(done)} of {case.num_seqs} prompts")
+                host = host_info()
                 entry["cpu_baseline"] = {
                     "value": round(sub_flops / wall / 1e12, 6), "unit": "TFLOP/s",
-                    "cores": max(1, math.ceil(cpu / wall)), "kind": "oracle",
+                    "cores": min(blas_threads(host), host["affinity_cpus"]), "kind": "oracle",
+                    "host": host, "avg_busy_threads": round(cpu / wall, 2),
                     "sample": f"{what} ({sum(done)} query rows), all 32 heads, fp64 numpy, "
                               f"{wall:.1f} s"}
             extra["causal-bf16-prefill"] = entry

@@ -422,6 +422,20 @@ int pa_profiler_enable(int on);
 void pa_profiler_reset(void);
 /* Returns PA_OK and fills total_ms / launches (0 if the name never ran). */
 int pa_profiler_read(const char* kernel, double* total_ms, int64_t* launches);
+/* Copies up to `max` of the kernel's per-launch durations (ms, launch order)
+ * since the last reset into ms[]; returns how many (>= 0) or a PA_ERR_*. */
+int64_t pa_profiler_samples(const char* kernel, float* ms, int64_t max);
+
+/*
+ * pa_clock_probe -- measures the shader clock while other work runs: one
+ * wave on `stream` waits `ticks` ticks of the GPU's 100 MHz reference
+ * counter (1 .. 10^8) and writes, to the device array out[2] (int64,
+ * 8-byte aligned), the shader clock ticks (out[0]) and reference ticks
+ * (out[1]) that passed; shader MHz = 100 * out[0] / out[1].  Asynchronous;
+ * a measurement aid for the benchmark (the achieved fraction of the MFMA
+ * peak at the clock the chip actually ran).
+ */
+int pa_clock_probe(int32_t ticks, int64_t* out, void* stream);
 
 #ifdef __cplusplus
 }

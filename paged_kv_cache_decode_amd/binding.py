@@ -50,7 +50,8 @@ _lib = None
 
 EXPORTS = ("pa_decode", "pa_decode_noalloc", "pa_decode_shared_prefix", "pa_prefill", "pa_write_kv", "pa_copy_blocks", "pa_status_string",
            "pa_last_error", "pa_decode_plan", "pa_workspace_release", "pa_profiler_enable",
-           "pa_profiler_reset", "pa_profiler_read", "pa_bm_create", "pa_bm_destroy",
+           "pa_profiler_reset", "pa_profiler_read", "pa_profiler_samples",
+           "pa_clock_probe", "pa_bm_create", "pa_bm_destroy",
            "pa_bm_num_free", "pa_bm_refcount", "pa_bm_add", "pa_bm_fork", "pa_bm_append",
            "pa_bm_take_copies", "pa_bm_free", "pa_bm_block_table")
 
@@ -77,6 +78,11 @@ def lib():
     L.pa_decode_plan.argtypes = [P, P, P, P, P, P, ctypes.POINTER(PaDecodePlanInfo)]
     L.pa_workspace_release.argtypes = [ctypes.c_void_p]
     L.pa_copy_blocks.argtypes = [P, P, P, P, ctypes.c_void_p]
+    L.pa_profiler_samples.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_float),
+                                      ctypes.c_int64]
+    L.pa_profiler_samples.restype = ctypes.c_int64
+    L.pa_clock_probe.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.pa_clock_probe.restype = ctypes.c_int
     V, I32P, I64P = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     L.pa_bm_create.argtypes = [ctypes.c_int32, ctypes.c_int32]
     L.pa_bm_create.restype = V
@@ -330,6 +336,14 @@ def workspace_release(stream=None):
     _check(lib().pa_workspace_release(_stream(stream)))
 
 
+def clock_probe(out, ticks: int = 20000, stream=None):
+    """Launch pa_clock_probe writing into ``out`` (int64 [2] on the GPU);
+    shader MHz = 100 * out[0] / out[1] once the stream has run it."""
+    if out.dtype != torch.int64 or out.numel() < 2 or not out.is_cuda:
+        raise ValueError("out must be a GPU int64 tensor of 2 elements")
+    _check(lib().pa_clock_probe(int(ticks), ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+
+
 def profiler_enable(on: bool = True):
     lib().pa_profiler_enable(1 if on else 0)
 
@@ -344,6 +358,18 @@ def profiler_read(kernel: str):
     n = ctypes.c_int64()
     _check(lib().pa_profiler_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def profiler_samples(kernel: str):
+    """Per-launch durations (ms, launch order) recorded for a kernel name."""
+    _, n = profiler_read(kernel)
+    if n == 0:
+        return []
+    buf = (ctypes.c_float * n)()
+    got = lib().pa_profiler_samples(kernel.encode(), buf, n)
+    if got < 0:
+        _check(int(got))
+    return list(buf[:got])
 
 
 class PreparedDecode:

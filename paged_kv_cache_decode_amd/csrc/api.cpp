@@ -55,6 +55,7 @@ std::vector<PendingTiming> g_pending;
 struct Total {
   double ms = 0;
   int64_t launches = 0;
+  std::vector<float> samples;  // each launch's duration, in launch order
 };
 std::map<std::string, Total> g_totals;
 
@@ -66,6 +67,7 @@ void drain_pending_locked() {
       Total& t = g_totals[p.name];
       t.ms += ms;
       t.launches += 1;
+      t.samples.push_back(ms);
     }
     (void)hipEventDestroy(p.start);
     (void)hipEventDestroy(p.stop);
@@ -490,6 +492,18 @@ int pa_copy_blocks(const pa_tensor* k_pool, const pa_tensor* v_pool, const pa_te
   return PA_OK;
 }
 
+int pa_clock_probe(int32_t ticks, int64_t* out, void* stream_ptr) {
+  g_last_error.clear();
+  if (!out) return set_error(PA_ERR_NULL, "out is NULL");
+  if (ticks < 1 || ticks > 100000000)
+    return set_error(PA_ERR_ARG, "ticks must be in 1 .. 10^8 (100 MHz reference ticks)");
+  if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0)
+    return set_error(PA_ERR_STRIDE, "out must be 8-byte aligned");
+  const hipError_t e = pa::launch_clock_probe(ticks, out, static_cast<hipStream_t>(stream_ptr));
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "clock probe: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 int pa_profiler_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
@@ -510,6 +524,19 @@ int pa_profiler_read(const char* kernel, double* total_ms, int64_t* launches) {
   *total_ms = it == g_totals.end() ? 0.0 : it->second.ms;
   *launches = it == g_totals.end() ? 0 : it->second.launches;
   return PA_OK;
+}
+
+int64_t pa_profiler_samples(const char* kernel, float* ms, int64_t max) {
+  if (!kernel || (max > 0 && !ms)) return set_error(PA_ERR_NULL, "NULL argument");
+  if (max < 0) return set_error(PA_ERR_ARG, "max must be >= 0");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending_locked();
+  auto it = g_totals.find(kernel);
+  if (it == g_totals.end()) return 0;
+  const std::vector<float>& v = it->second.samples;
+  const int64_t n = std::min<int64_t>(max, (int64_t)v.size());
+  std::copy(v.begin(), v.begin() + n, ms);
+  return n;
 }
 
 }  // extern "C"

@@ -31,6 +31,10 @@ hipError_t launch_write_kv(const WriteKvPlan& plan, hipStream_t stream);
 
 hipError_t launch_copy_blocks(const CopyBlocksPlan& plan, hipStream_t stream);
 
+// Shader-clock probe (pa_clock_probe): out[0] = shader clock ticks, out[1] =
+// 100 MHz reference ticks over one wave's wait of `ticks` reference ticks.
+hipError_t launch_clock_probe(int64_t ticks, int64_t* out, hipStream_t stream);
+
 // Kernel timer.  While the profiler is enabled, a KernelTimer holds a pair
 // of events that timed_launch (launch.h) binds to one kernel dispatch; the
 // pair is queued for reading by commit() and released otherwise.

@@ -92,6 +92,25 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
   *reinterpret_cast<u32x4_t*>(a.vp + to) = load16(a.vp + from);
 }
 
+// Shader-clock probe: one wave reads the shader clock counter (s_memtime)
+// and the 100 MHz reference counter (s_memrealtime) at its start and once
+// `ticks` reference ticks have passed (the loop ends on elapsed real time,
+// whatever else the chip is doing), and stores both deltas.
+__global__ __launch_bounds__(64) void clock_probe_kernel(int64_t ticks, int64_t* out) {
+  const int64_t r0 = (int64_t)__builtin_amdgcn_s_memrealtime();
+  const int64_t c0 = (int64_t)__builtin_amdgcn_s_memtime();
+  int64_t r = r0;
+  while (r - r0 < ticks) {
+    __builtin_amdgcn_s_sleep(2);
+    r = (int64_t)__builtin_amdgcn_s_memrealtime();
+  }
+  const int64_t c1 = (int64_t)__builtin_amdgcn_s_memtime();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r - r0;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_copy_blocks(const CopyBlocksPlan& pl, hipStream_t stream) {
@@ -105,6 +124,11 @@ hipError_t launch_copy_blocks(const CopyBlocksPlan& pl, hipStream_t stream) {
   if (a.total == 0) return hipSuccess;
   return timed_launch("copy_blocks", copy_blocks_kernel, dim3((unsigned)((a.total + 255) / 256)),
                       dim3(256), stream, a);
+}
+
+hipError_t launch_clock_probe(int64_t ticks, int64_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, stream, ticks, out);
+  return hipGetLastError();
 }
 
 }  // namespace pa

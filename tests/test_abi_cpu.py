@@ -276,3 +276,18 @@ def test_decode_noalloc_rejects_what_its_fixed_workspace_cannot_hold(monkeypatch
     assert "fixed workspace" in L.pa_last_error().decode()
     monkeypatch.setenv("PA_DECODE_WORKERS", "100000")  # 100,032 partial slots of 2,064 bytes
     assert call(decode_args()) == -6
+
+
+def test_measurement_aids_reject_bad_arguments():
+    """pa_clock_probe and pa_profiler_samples check their arguments before
+    any device work; the profiler reads need no GPU."""
+    L = B.lib()
+    assert L.pa_clock_probe(1000, None, None) == -1
+    assert L.pa_clock_probe(0, ctypes.c_void_p(FAKE), None) == -8
+    assert L.pa_clock_probe(100000001, ctypes.c_void_p(FAKE), None) == -8
+    assert L.pa_clock_probe(1000, ctypes.c_void_p(FAKE + 4), None) == -4
+    assert L.pa_profiler_samples(b"decode_partitions", None, 4) == -1
+    buf = (ctypes.c_float * 4)()
+    assert L.pa_profiler_samples(b"decode_partitions", buf, -1) == -8
+    assert L.pa_profiler_samples(b"no_such_kernel", buf, 4) == 0
+    assert B.profiler_samples("no_such_kernel") == []
