@@ -56,8 +56,9 @@
  *     included).
  *   - Graph capture: pa_decode, pa_decode_shared_prefix, pa_prefill,
  *     pa_write_kv and pa_copy_blocks issue only kernel launches once a
- *     decode call's workspace exists, so they can be captured into a HIP
- *     graph and replayed (a replay reads the buffers' contents at replay
+ *     decode call's workspace exists (pa_decode_shared_prefix also records
+ *     and waits on the events that fork its second stream and join it
+ *     back), so they can be captured into a HIP graph and replayed (a replay reads the buffers' contents at replay
  *     time).  A decode call that would have to grow its stream's workspace
  *     during a capture returns PA_ERR_ALLOC instead: make one call of the
  *     same (or larger) size on that stream before capturing.  A graph uses
@@ -275,10 +276,16 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
  *      as one dense block on the matrix cores (the prefill kernel, keys
  *      split into at most 4 chunks), giving normalised partial outputs and
  *      log-sum-exps;
- *   2. the decode kernel attends each sequence's own keys
- *      [prefix_len, n_s), starting each (sequence, KV head) from the
- *      log-sum-exp merge of its prefix chunks, and merges its own parts as
- *      pa_decode does, writing `out`.
+ *   2. concurrently, the decode kernel attends each sequence's own keys
+ *      [prefix_len, n_s) and merges its own parts as pa_decode does, into
+ *      an f32 state (output and log-sum-exp) in the workspace;
+ *   3. a join kernel merges, per (sequence, head), the prefix chunks with
+ *      that state (log-sum-exp merge) and writes `out`.
+ * Step 1 runs on a second stream of default priority that the library
+ * makes at the first call on `stream` and keeps with the stream's workspace
+ * (pa_workspace_release destroys it); events order it after the work
+ * already queued on `stream` and order step 3 after it, so the call is
+ * stream-ordered on `stream` like every other call.
  *
  *   prefix_len   host int, a multiple of the block size, 0 <= prefix_len
  *                <= MB * B.  0 is plain pa_decode.
@@ -287,7 +294,10 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
  * Supported: f16/bf16, d = 128 (other shapes return PA_ERR_UNSUPPORTED);
  * the same G, B and strides as pa_decode.  The workspace (see pa_decode)
  * also holds the prefix parts, n_chunks * S * H * (d + 1) * 4 bytes, where
- * n_chunks <= min(4, ceil(prefix_len / 64)).
+ * n_chunks <= min(4, ceil(prefix_len / 64)), and the suffix state,
+ * S * H * (d + 1) * 4 bytes.  Graph capture: as for the workspace, the
+ * second stream must exist (one call on `stream` before capturing); the
+ * captured graph then holds the fork and the join.
  */
 int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
                             const pa_tensor* v_pool, const pa_tensor* block_table,

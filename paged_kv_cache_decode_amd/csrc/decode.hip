@@ -18,14 +18,19 @@
 // order), form one list in which a unit takes kUnitCost places for starting
 // it (fetching Q, refilling the load pipeline, writing its result) and then
 // one place per tile: `total` places.  The kernel launches W wavefronts
-// ("workers", one workgroup of four per compute unit) and gives worker i the
-// tiles at places [i*q, (i+1)*q) of the list, q = ceil(total / W), so every
-// worker does about the same work whatever the mix of context lengths -- no
-// tail of long partitions, no idle XCD; a worker that starts more units gets
-// fewer tiles.  Worker numbers are dealt so that each of the 8 XCDs (which receive
-// workgroups round-robin) owns one contiguous eighth of the list: with
-// head-major order an XCD then serves one or two KV heads, and K/V blocks
-// that several sequences share (a common prompt prefix) stay in its L2.
+// ("workers", one workgroup of four per compute unit) and cuts each KV
+// head's part of the list into W / Hkv equal slices (or, when Hkv does not
+// divide W, the whole list into W equal slices), so every worker does about
+// the same work whatever the mix of context lengths -- no tail of long
+// partitions, no idle XCD; a worker that starts more units gets fewer
+// tiles.  Slice j of every head covers the same sequences and tiles; two
+// workers of one workgroup take slice j of two adjacent heads, so their
+// waves read neighbouring 256-byte segments of the same token rows
+// together.  Worker numbers are dealt so that each of the 8 XCDs (which
+// receive workgroups round-robin) owns a contiguous run of them: with 8 KV
+// heads an XCD serves one pair of heads over half of the sequences, and K/V
+// blocks that several of those sequences share (a common prompt prefix)
+// stay in its L2.
 // The piece of a unit that one worker covers is a partition: a worker that
 // covers a whole unit writes `out` directly; otherwise it writes a
 // normalised partial output and its log2-sum-exp and counts itself in the
@@ -108,17 +113,10 @@ struct DecodeArgs {
   uint32_t tok_bytes;
   int64_t head_bytes;
   float scale_log2;  // scale * log2(e)
-  // Shared prefix (cascade): keys [0, key_begin) of every sequence were
-  // attended by an earlier kernel in n_pre key chunks, whose normalised
-  // partial results are pre_o [n_pre, H, S, D] with log2-sum-exp pre_lse
-  // [n_pre, H, S].  This kernel attends keys [key_begin, n_s): the first
-  // piece of each unit merges the chunks (log-sum-exp) and starts its online
-  // softmax from that state instead of from zero.  key_begin = 0 and
-  // pre_o = nullptr for plain decode.
+  // Keys attended per sequence: [key_begin, n_s).  key_begin = 0 for plain
+  // decode; the suffix step of a shared-prefix decode starts after the
+  // prefix, whose keys another kernel attends.
   int key_begin;
-  int n_pre;
-  const float* pre_o;
-  const float* pre_lse;
   // Optional natural-log log-sum-exp per (s, query head): lse_out[s *
   // lse_ss + h], or nullptr.
   float* lse_out;
@@ -248,56 +246,6 @@ __device__ __forceinline__ float load_partial(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The shared prefix's merged state for unit (s, g), from its n_pre key
-// chunks, computed by the whole wave: lane l owns kV = G*D/64 consecutive
-// values of the unit's [G][D] output.
-//   M = max_c lse_c,  W = sum_c 2^(lse_c - M)  (the prefix's softmax sum
-//   relative to M),  o = sum_c 2^(lse_c - M) o_c  (unnormalised, relative
-//   to M),
-// for the lane's head (M, W) and values (o).  Loading (all chunks' loads in
-// flight together) and merging are separate steps, so that other loads can
-// be issued in between.
-template <int D, int G>
-struct PrefixParts {
-  static constexpr int kV = G * D / 64;
-  float lse[kMaxPrefixChunks];
-  float ov[kMaxPrefixChunks][kV];
-
-  __device__ __forceinline__ void load(const DecodeArgs& a, int s, int g, int lane) {
-    const int idx0 = lane * kV;
-    const int hq = g * G + idx0 / D, d0 = idx0 % D;
-#pragma unroll
-    for (int c = 0; c < kMaxPrefixChunks; ++c) {
-      if (c < a.n_pre) {
-        const int64_t row = ((int64_t)c * a.H + hq) * a.S + s;
-        lse[c] = a.pre_lse[row];
-#pragma unroll
-        for (int e = 0; e < kV; ++e) ov[c][e] = a.pre_o[row * D + d0 + e];
-      } else {
-        lse[c] = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < kV; ++e) ov[c][e] = 0.f;
-      }
-    }
-  }
-
-  __device__ __forceinline__ void merge(float& M, float& W, float* o) const {
-    M = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < kMaxPrefixChunks; ++c) M = fmaxf(M, lse[c]);
-    W = 0.f;
-#pragma unroll
-    for (int e = 0; e < kV; ++e) o[e] = 0.f;
-#pragma unroll
-    for (int c = 0; c < kMaxPrefixChunks; ++c) {
-      const float w = lse[c] == -INFINITY ? 0.f : fast_exp2(lse[c] - M);
-      W += w;
-#pragma unroll
-      for (int e = 0; e < kV; ++e) o[e] = fmaf(w, ov[c][e], o[e]);
-    }
-  }
-};
-
 // Log-sum-exp merge of the np partitions of unit (g, s), held in slots
 // slot0 .. slot0+np-1, by one wave:
 //   out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),  M = max_p lse_p,
@@ -357,34 +305,18 @@ __device__ __forceinline__ void merge_unit(const DecodeArgs& a, int g, int s, in
 }
 
 // Units with no key to attend here are in no worker's slice: their output
-// is zero, or, with a shared prefix, the prefix's merged parts.  Worker i
-// writes units i, i + W, ... (after its own slice, so that the check is off
-// the path to the first K/V loads).
+// is zero (and their log-sum-exp -inf).  Worker i writes units i, i + W, ...
+// (after its own slice, so that the check is off the path to the first K/V
+// loads).
 template <class T, int D, int G>
 __device__ __forceinline__ void zero_empty_units(const DecodeArgs& a, int worker, int lane) {
   for (int u = worker; u < a.S * a.Hkv; u += a.W) {
     const int su = u % a.S, gu = u / a.S;
     if (as_const(a.cl)[su] <= a.key_begin) {
-      if (a.pre_o) {
-        // Only the shared prefix: its merged chunks are the whole result.
-        constexpr int kV = G * D / 64;
-        float M, W, o[kV];
-        PrefixParts<D, G> pp;
-        pp.load(a, su, gu, lane);
-        pp.merge(M, W, o);
-        const float inv = W > 0.f ? 1.f / W : 0.f;
-        const int idx0 = lane * kV;
-#pragma unroll
-        for (int e = 0; e < kV; ++e)
-          store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + idx0 / D) * a.o_sh +
-                                  idx0 % D + e,
-                       o[e] * inv, a.out_f32 != 0);
-      } else {
-        for (int i = lane; i < G * D; i += 64)
-          store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
-                       0.f, a.out_f32 != 0);
-        if (a.lse_out && lane < G) a.lse_out[(int64_t)su * a.lse_ss + gu * G + lane] = -INFINITY;
-      }
+      for (int i = lane; i < G * D; i += 64)
+        store_out<T>(a.out, (int64_t)su * a.o_ss + (int64_t)(gu * G + i / D) * a.o_sh + i % D,
+                     0.f, a.out_f32 != 0);
+      if (a.lse_out && lane < G) a.lse_out[(int64_t)su * a.lse_ss + gu * G + lane] = -INFINITY;
     }
   }
 }
@@ -412,7 +344,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   if (worker >= a.W) return;
 
   __shared__ float p_lds[kNW][kTileKeys][G > 4 ? G : 4];
-  __shared__ float seed_lds[kNW][G * D];  // shared-prefix seed, per wave
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kNW][G * Geo::kRowBytes];
   // K tile in the MFMA operand layout (kKRows): rows padded by 16 bytes, so
   // that the 16 rows one read instruction covers start on different banks.
@@ -434,9 +365,29 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
   // Positions below are in cost units: a unit occupies its start cost, then
   // one unit per tile.
   const int64_t total = t_all * a.Hkv;
-  const int64_t per = (total + a.W - 1) / a.W;
-  const int64_t begin = (int64_t)worker * per;
-  const int64_t end = min(total, begin + per);
+  // When W is a multiple of Hkv, each KV head's sublist is cut into
+  // wh = W / Hkv equal slices, so that slice j of every head covers the same
+  // (sequence, tile) range.  Workers are dealt in pairs over adjacent heads
+  // (worker 2i and 2i+1: slice j of heads 2p and 2p+1), so the two waves
+  // read adjacent 256-byte head segments of the same token rows at about the
+  // same time; consecutive pairs take consecutive j.  Slice number sl (which
+  // names the partial-result slots) is head * wh + j.  Measured against one
+  // head per run of workers: gqa-f16-decode 97.3 -> 91.9 us,
+  // long-bf16-decode 273.5 -> 255 us (groups of all 8 heads per pair of
+  // workgroups measured the same on those and lost more of the L2 reuse of
+  // blocks shared between sequences).  With W not a multiple of Hkv, or an
+  // odd Hkv, the list is cut into W equal slices in worker order.
+  const bool aligned = a.W % a.Hkv == 0;
+  const int wh = aligned ? a.W / a.Hkv : a.W;
+  const int64_t per = aligned ? (t_all + wh - 1) / wh : (total + a.W - 1) / a.W;
+  const int pair = a.Hkv % 2 == 0 ? 2 : 1;
+  const int gw = (worker / (pair * wh)) * pair + worker % pair;  // this worker's head
+  const int sl = aligned ? gw * wh + (worker / pair) % wh : worker;
+  const int64_t hbase = aligned ? (int64_t)gw * t_all : 0;
+  const int64_t hend = aligned ? hbase + t_all : total;
+  const int64_t begin = aligned ? min(hend, hbase + (int64_t)(sl % wh) * per)
+                                : (int64_t)worker * per;
+  const int64_t end = min(hend, begin + per);
   if (begin >= end) {
     zero_empty_units<T, D, G>(a, worker, lane);
     return;
@@ -648,39 +599,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
     // issues one tile's loads per computed tile (fixed waits); an epilogue
     // finishes the last 1 .. 2*kDepth-1 tiles without loading past the end.
     // The first loads are clamped to the last tile of a short partition.
-    // A unit's first piece with a shared prefix loads the prefix's chunk
-    // parts before the first K/V tiles and merges them while those are in
-    // flight.
-    const bool seed = a.pre_o && j0 == 0;
-    PrefixParts<D, G> parts;
-    if (seed) parts.load(a, s, g, lane);
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) load_tile(i, kr[i], vr[i]);
-    if (seed) {
-      // The unit's first piece continues the shared prefix's softmax: the
-      // merged state of its key chunks (max M, sum W, output) enters once --
-      // the sum in one lane of each 16-lane row (rows are summed at the
-      // end), the output in the lanes of V row 0 (lanes sharing a column
-      // are summed at the end).  The merged values reach the accumulator
-      // layout through this wave's LDS slot.
-      constexpr int kV = G * D / 64;
-      float M, W, o[kV];
-      parts.merge(M, W, o);
-#pragma unroll
-      for (int e = 0; e < kV; ++e) seed_lds[w][lane * kV + e] = o[e];
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        m[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), h * D / kV));
-        const float Wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(W), h * D / kV));
-        l_lane[h] = r16 == 0 ? Wh : 0.f;
-        if (lane < Geo::kLPR) {
-#pragma unroll
-          for (int e = 0; e < kE; ++e) acc[h][e] = seed_lds[w][h * D + lane * kE + e];
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
 #pragma unroll
     for (int j = 0; j < kQPer; ++j)
       if (lane + 64 * j < kQChunks) *reinterpret_cast<u32x4_t*>(my_q + (lane + 64 * j) * 16) = qreg[j];
@@ -726,7 +646,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
             store_out<T>(a.out, (int64_t)s * a.o_ss + (int64_t)(hq0 + h) * a.o_sh + lane * kE + e,
                          acc[h][e] * inv, a.out_f32 != 0);
         } else {
-          store_partial_row<kE, Geo::kLPR>(a.part_o + ((int64_t)(worker + u) * G + h) * D, lane,
+          store_partial_row<kE, Geo::kLPR>(a.part_o + ((int64_t)(sl + u) * G + h) * D, lane,
                                            acc[h], inv);
         }
       }
@@ -740,11 +660,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partitions_kernel(De
       if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
-          store_partial(a.part_lse + (int64_t)(worker + u) * G + h, m[h] + __log2f(l_lane[h]));
+          store_partial(a.part_lse + (int64_t)(sl + u) * G + h, m[h] + __log2f(l_lane[h]));
       }
-      // Workers first .. last hold the unit's partitions (slots worker + u).
-      const int first = (int)(tile0 / per);
-      const int last = (int)((tile0 + ts - 1) / per);
+      // Slices first .. last hold the unit's partitions (slots first + u ..).
+      const int64_t h0 = aligned ? (int64_t)g * t_all : 0;  // this head's sublist start
+      const int sl0 = aligned ? g * wh : 0;
+      const int first = sl0 + (int)((tile0 - h0) / per);
+      const int last = sl0 + (int)((tile0 + ts - 1 - h0) / per);
       // Once this wave's partial stores have completed, count the partition;
       // the worker that brings the count to the number of partitions merges
       // them and leaves the counter at zero.
@@ -773,7 +695,7 @@ hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   // whole rows; with groups of 8 that instance would spill registers, so
   // those keep the operand-layout loads.
   if constexpr (D == 128 && !__is_same(T, TF32) && G <= 4) {
-    if (pl.pre_o)
+    if (pl.key_begin > 0)
       return timed_launch("decode_partitions", decode_partitions_kernel<T, D, G, true>,
                           dim3((unsigned)pl.grid[0]), dim3(pl.block_threads), stream, a);
   }
@@ -929,9 +851,6 @@ hipError_t launch_decode(const DecodePlan& pl, void* workspace, hipStream_t stre
   a.head_bytes = pl.pool.head * e;
   a.scale_log2 = pl.scale * 1.4426950408889634f;
   a.key_begin = pl.key_begin;
-  a.n_pre = pl.n_pre;
-  a.pre_o = pl.pre_o;
-  a.pre_lse = pl.pre_lse;
   a.lse_out = pl.lse;
   a.lse_ss = pl.lse_ss;
   switch (pl.dtype) {
@@ -1048,6 +967,98 @@ hipError_t launch_merge(const MergePlan& pl, hipStream_t stream) {
                                    stream, a)
                     : timed_launch("merge_states", merge_states_kernel<128>, grid, dim3(256),
                                    stream, a);
+}
+
+namespace {
+
+// The last step of a shared-prefix decode: for each (s, h) the parts are the
+// prefix's key chunks and the state of the sequence's own keys; with
+// lse in log2 units, M = max_p lse_p and w_p = 2^(lse_p - M),
+//   out = sum_p w_p o_p / sum_p w_p
+// (the same whole-part rescaling as merge_states_kernel).  One wavefront per
+// (s, h), lane l holding values l*kV .. l*kV+kV-1; all parts' loads are
+// issued before any is used.
+struct PrefixJoinArgs {
+  const float* pre_o;
+  const float* pre_lse;
+  const float* suf_o;
+  const float* suf_lse;
+  void* out;
+  int64_t o_ss, o_sh;
+  int out_dtype;
+  int n_pre, S, H;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prefix_join_kernel(PrefixJoinArgs a) {
+  constexpr int kV = D / 64;
+  constexpr int kP = kMaxPrefixChunks + 1;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (unit >= (int64_t)a.S * a.H) return;
+  const int s = (int)(unit / a.H), h = (int)(unit % a.H);
+  float l[kP], o[kP][kV];
+#pragma unroll
+  for (int c = 0; c < kMaxPrefixChunks; ++c) {
+    const bool in = c < a.n_pre;
+    const int64_t row = ((int64_t)c * a.H + h) * a.S + s;
+    l[c] = in ? a.pre_lse[row] : -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kV; ++e) o[c][e] = in ? a.pre_o[row * D + lane * kV + e] : 0.f;
+  }
+  l[kP - 1] = a.suf_lse[unit] * 1.4426950408889634f;  // natural log -> log2
+#pragma unroll
+  for (int e = 0; e < kV; ++e) o[kP - 1][e] = a.suf_o[unit * D + lane * kV + e];
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kP; ++p) M = fmaxf(M, l[p]);
+  float acc[kV], wsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < kV; ++e) acc[e] = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      if (l[p] == -INFINITY) continue;  // a part with no keys
+      const float w = fast_exp2(l[p] - M);
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < kV; ++e) acc[e] = fmaf(w, o[p][e], acc[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t ob = (int64_t)s * a.o_ss + (int64_t)h * a.o_sh + lane * kV;
+#pragma unroll
+  for (int e = 0; e < kV; ++e) {
+    const float v = acc[e] * inv;
+    if (a.out_dtype == PA_F32)
+      static_cast<float*>(a.out)[ob + e] = v;
+    else if (a.out_dtype == PA_F16)
+      static_cast<uint16_t*>(a.out)[ob + e] = to_f16_bits(v);
+    else
+      static_cast<uint16_t*>(a.out)[ob + e] = to_bf16_bits(v);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefix_join(const PrefixJoinPlan& pl, hipStream_t stream) {
+  PrefixJoinArgs a;
+  a.pre_o = pl.pre_o;
+  a.pre_lse = pl.pre_lse;
+  a.suf_o = pl.suf_o;
+  a.suf_lse = pl.suf_lse;
+  a.out = pl.out;
+  a.o_ss = pl.o_ss;
+  a.o_sh = pl.o_sh;
+  a.out_dtype = pl.out_dtype;
+  a.n_pre = pl.n_pre;
+  a.S = pl.S;
+  a.H = pl.H;
+  const int64_t units = (int64_t)pl.S * pl.H;
+  if (units == 0) return hipSuccess;
+  if (pl.D != 128 || pl.n_pre > kMaxPrefixChunks) return hipErrorInvalidValue;
+  return timed_launch("prefix_join", prefix_join_kernel<128>, dim3((unsigned)((units + 3) / 4)),
+                      dim3(256), stream, a);
 }
 
 }  // namespace pa

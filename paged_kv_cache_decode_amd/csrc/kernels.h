@@ -27,6 +27,9 @@ hipError_t launch_prefill(const PrefillPlan& plan, hipStream_t stream);
 // Joins partial attention states (pa_merge_states).
 hipError_t launch_merge(const MergePlan& plan, hipStream_t stream);
 
+// Joins a shared prefix's key chunks with the suffix step's state.
+hipError_t launch_prefix_join(const PrefixJoinPlan& plan, hipStream_t stream);
+
 hipError_t launch_write_kv(const WriteKvPlan& plan, hipStream_t stream);
 
 hipError_t launch_copy_blocks(const CopyBlocksPlan& plan, hipStream_t stream);

@@ -56,13 +56,9 @@ struct DecodePlan {
   void* out = nullptr;
   int64_t o_ss = 0, o_sh = 0;
   float scale = 0.f;
-  // Shared prefix: keys [0, key_begin) were attended by the prefix step in
-  // n_pre key chunks, whose partial results are pre_o [n_pre, H, S, D] /
-  // pre_lse [n_pre, H, S].
+  // Keys attended per sequence: [key_begin, n_s) (the suffix step of
+  // pa_decode_shared_prefix starts after the prefix; 0 otherwise).
   int key_begin = 0;
-  int n_pre = 0;
-  const float* pre_o = nullptr;
-  const float* pre_lse = nullptr;
   // Optional natural-log log-sum-exp of each (sequence, query head),
   // lse[s * lse_ss + h] (pa_decode_lse).
   float* lse = nullptr;
@@ -149,6 +145,21 @@ struct MergePlan {
   int64_t o_s = 0, o_h = 0;
   float* lse = nullptr;             // optional [S, H]
   int64_t l_s = 0, l_h = 0;
+};
+
+// Last step of pa_decode_shared_prefix: the prefix's key chunks
+// (pre_o [n_pre, H, S, D], log2-sum-exp pre_lse [n_pre, H, S]) joined with
+// the suffix step's state (suf_o [S, H, D] normalised, natural-log
+// suf_lse [S, H]) into out.
+struct PrefixJoinPlan {
+  int S = 0, H = 0, D = 0, n_pre = 0;
+  const float* pre_o = nullptr;
+  const float* pre_lse = nullptr;
+  const float* suf_o = nullptr;
+  const float* suf_lse = nullptr;
+  void* out = nullptr;
+  int out_dtype = 0;
+  int64_t o_ss = 0, o_sh = 0;
 };
 
 struct CopyBlocksPlan {
