@@ -83,7 +83,8 @@ def parse():
 
 # Headers every kernel source includes; a change in any of them can change
 # the compiled kernels, so they enter every kernel's source hash.
-SHARED_HEADERS = ("device_common.h", "kernels.h", "launch.h", "plan.h")
+SHARED_HEADERS = ("device_common.h", "kernels.h", "launch.h", "plan.h", "decode_kernel.h",
+                  "prefill_kernel.h")
 
 
 def source_hash(*names):
@@ -111,15 +112,14 @@ def load_traffic(kernel, workload, src_hash, bytes_per_launch):
 
 # Kernel record name -> (substring of its demangled symbol, source).  The
 # last three tell apart the kernels of the prefix-shared workload: plain
-# decode, and the shared-prefix call's prefix step (the prefill kernel with
-# one 16-row wave per head) and suffix step (whole-row K).
+# decode, and the shared-prefix call's two kernels (prefix and suffix steps
+# in one kernel, then the join).
 KERNEL_SOURCES = {"decode_partitions": ("decode_partitions_kernel", "decode.hip"),
                   "prefill": ("prefill_kernel", "prefill.hip"),
                   "decode_partitions_plain":
                       ("decode_partitions_kernel<pa::TBF16, 128, 4, false>", "decode.hip"),
-                  "decode_partitions_suffix":
-                      ("decode_partitions_kernel<pa::TBF16, 128, 4, true>", "decode.hip"),
-                  "prefill_prefix": ("prefill_kernel<pa::TBF16, 4, 1>", "prefill.hip")}
+                  "shared_prefix": ("shared_prefix_kernel", "shared_prefix.hip"),
+                  "prefix_join": ("prefix_join_kernel", "decode.hip")}
 COPY_CALIBRATION_BYTES = 1 << 30
 
 
@@ -200,23 +200,23 @@ def prefix_dram_measured(unique):
     (rocprofv3 counter records, if taken on the current sources), against
     the unique bytes the method must move."""
     wl = "prefix-shared-bf16-decode-B16"
-    dec, pre = source_hash("decode.hip"), source_hash("prefill.hip")
+    dec, sp = source_hash("decode.hip"), source_hash("shared_prefix.hip")
     plain = load_traffic("decode_partitions_plain", wl, dec, unique)
-    prefix = load_traffic("prefill_prefix", wl, pre, unique)
-    suffix = load_traffic("decode_partitions_suffix", wl, dec, unique)
+    comb = load_traffic("shared_prefix", wl, sp, unique)
+    join = load_traffic("prefix_join", wl, dec, unique)
     out = {"plain_decode": None, "shared_prefix_call": None}
     if plain:
         out["plain_decode"] = {"fetch_bytes": plain["fetch_bytes"],
                                "write_bytes": plain["write_bytes"],
                                "over_unique": plain["ratio_to_algorithmic"]}
-    if prefix and suffix:
-        tot = (prefix["fetch_bytes"] + prefix["write_bytes"] + suffix["fetch_bytes"] +
-               suffix["write_bytes"])
+    if comb and join:
+        tot = (comb["fetch_bytes"] + comb["write_bytes"] + join["fetch_bytes"] +
+               join["write_bytes"])
         out["shared_prefix_call"] = {
-            "prefix_step": {"fetch_bytes": prefix["fetch_bytes"],
-                            "write_bytes": prefix["write_bytes"]},
-            "suffix_step": {"fetch_bytes": suffix["fetch_bytes"],
-                            "write_bytes": suffix["write_bytes"]},
+            "prefix_and_suffix_kernel": {"fetch_bytes": comb["fetch_bytes"],
+                                         "write_bytes": comb["write_bytes"]},
+            "join_kernel": {"fetch_bytes": join["fetch_bytes"],
+                            "write_bytes": join["write_bytes"]},
             "over_unique": round(tot / unique, 4)}
     return out
 
@@ -337,9 +337,9 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
     timer.run(step, steps)
     binding.profiler_enable(False)
     part_ms, part_n = kernel_avg_ms(binding, "decode_partitions")
-    pre_ms, pre_n = kernel_avg_ms(binding, "prefill")
-    part_spread = kernel_spread(binding, "decode_partitions")
-    pre_spread = kernel_spread(binding, "prefill") if pre_n else None
+    part_spread = kernel_spread(binding, "decode_partitions") if part_n else None
+    comb_spread = kernel_spread(binding, "shared_prefix")
+    join_spread = kernel_spread(binding, "prefix_join")
     binding.profiler_reset()
     step_spread = spread_us(timer.step_times_ms(step, steps))
     del calls, devs
@@ -347,8 +347,8 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
     binding.workspace_release()
     torch.cuda.empty_cache()
     return dict(sec=sec, part_ms=part_ms, part_launches=part_n, plan=plan,
-                prefix_ms=pre_ms if pre_n else 0.0, part_spread=part_spread,
-                prefix_spread=pre_spread, step_spread=step_spread)
+                part_spread=part_spread, comb_spread=comb_spread, join_spread=join_spread,
+                step_spread=step_spread)
 
 
 def bench_long_share(torch, binding, W, steps):
@@ -598,10 +598,8 @@ def main():
                                                          HBM_PEAK_GBS, 4),
                         "ms_per_step": round(rc["sec"] * 1e3, 4),
                         "step_us": rc["step_spread"],
-                        "prefix_kernel_avg_us": round(rc["prefix_ms"] * 1e3, 2),
-                        "prefix_kernel_us": rc["prefix_spread"],
-                        "suffix_kernel_avg_us": round(rc["part_ms"] * 1e3, 2),
-                        "suffix_kernel_us": rc["part_spread"]},
+                        "prefix_and_suffix_kernel_us": rc["comb_spread"],
+                        "join_kernel_us": rc["join_spread"]},
                     "unique_bytes": unique, "logical_bytes": logical,
                     "config": {**workload_meta(case), "prefix_len": case.meta["prefix_len"]}}
                 if B == 16:

@@ -56,9 +56,8 @@
  *     included).
  *   - Graph capture: pa_decode, pa_decode_shared_prefix, pa_prefill,
  *     pa_write_kv and pa_copy_blocks issue only kernel launches once a
- *     decode call's workspace exists (pa_decode_shared_prefix also records
- *     and waits on the events that fork its second stream and join it
- *     back), so they can be captured into a HIP graph and replayed (a replay reads the buffers' contents at replay
+ *     decode call's workspace exists, so they can be captured into a HIP
+ *     graph and replayed (a replay reads the buffers' contents at replay
  *     time).  A decode call that would have to grow its stream's workspace
  *     during a capture returns PA_ERR_ALLOC instead: make one call of the
  *     same (or larger) size on that stream before capturing.  A graph uses
@@ -273,19 +272,15 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
  * the same math, up to floating-point rounding); the work is split so that
  * the prefix is read once per KV head instead of once per sequence:
  *   1. every sequence's G query heads attend to the prefix keys together,
- *      as one dense block on the matrix cores (the prefill kernel, keys
+ *      as one dense block on the matrix cores (prefill workgroups, keys
  *      split into at most 4 chunks), giving normalised partial outputs and
  *      log-sum-exps;
- *   2. concurrently, the decode kernel attends each sequence's own keys
- *      [prefix_len, n_s) and merges its own parts as pa_decode does, into
- *      an f32 state (output and log-sum-exp) in the workspace;
- *   3. a join kernel merges, per (sequence, head), the prefix chunks with
+ *   2. alongside, in the same kernel, decode workgroups attend each
+ *      sequence's own keys [prefix_len, n_s) and merge their parts as
+ *      pa_decode does, into an f32 state (output and log-sum-exp) in the
+ *      workspace;
+ *   3. a second kernel merges, per (sequence, head), the prefix chunks with
  *      that state (log-sum-exp merge) and writes `out`.
- * Step 1 runs on a second stream of default priority that the library
- * makes at the first call on `stream` and keeps with the stream's workspace
- * (pa_workspace_release destroys it); events order it after the work
- * already queued on `stream` and order step 3 after it, so the call is
- * stream-ordered on `stream` like every other call.
  *
  *   prefix_len   host int, a multiple of the block size, 0 <= prefix_len
  *                <= MB * B.  0 is plain pa_decode.
@@ -295,9 +290,7 @@ int pa_write_kv(const pa_tensor* k_new, const pa_tensor* v_new,
  * the same G, B and strides as pa_decode.  The workspace (see pa_decode)
  * also holds the prefix parts, n_chunks * S * H * (d + 1) * 4 bytes, where
  * n_chunks <= min(4, ceil(prefix_len / 64)), and the suffix state,
- * S * H * (d + 1) * 4 bytes.  Graph capture: as for the workspace, the
- * second stream must exist (one call on `stream` before capturing); the
- * captured graph then holds the fork and the join.
+ * S * H * (d + 1) * 4 bytes.
  */
 int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
                             const pa_tensor* v_pool, const pa_tensor* block_table,
@@ -424,9 +417,9 @@ int pa_decode_plan(const pa_tensor* q, const pa_tensor* k_pool, const pa_tensor*
  * elapsed time is the kernel's own execution.
  * pa_profiler_read synchronises on the recorded events and adds their
  * elapsed times to per-kernel totals.  Kernel names: "decode_partitions",
- * "prefill" (also the prefix step of pa_decode_shared_prefix), "write_kv",
- * "copy_blocks".  Not meant for concurrent use from
- * several threads.
+ * "prefill", "shared_prefix" and "prefix_join" (pa_decode_shared_prefix's
+ * two kernels), "merge_states", "write_kv", "copy_blocks".  Not meant for
+ * concurrent use from several threads.
  */
 int pa_profiler_enable(int on);
 void pa_profiler_reset(void);

@@ -24,7 +24,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "api.cpp", "block_manager.cpp", "decode.hip", "prefill.hip", "write_kv.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "block_manager.cpp", "decode.hip", "prefill.hip",
+           "shared_prefix.hip", "write_kv.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -167,11 +167,6 @@ struct StreamWorkspace {
   int64_t part_bytes = 0;     // capacity of the partial-result region
   bool captured = false;      // a capture on this stream recorded `ptr`
   std::vector<void*> retired; // superseded buffers that captured graphs use
-  // pa_decode_shared_prefix's second stream (default priority) and the two
-  // events that fork work onto it and join it back, made at its first call
-  // on this stream.
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, void*>, StreamWorkspace> g_ws;
@@ -219,40 +214,6 @@ int acquire_workspace(pa::DecodePlan* plan, hipStream_t stream, void** out) {
   if (pa::capturing(stream)) w.captured = true;
   plan->counter_bytes = w.counter_bytes;  // partials start after the counters
   *out = w.ptr;
-  return PA_OK;
-}
-
-// The side stream and fork/join events of the caller's stream (whose
-// workspace acquire_workspace has just made).  Created outside graph
-// capture only, like the workspace itself.
-int acquire_side(hipStream_t stream, hipStream_t* side, hipEvent_t* fork, hipEvent_t* join) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  StreamWorkspace& w = g_ws[{dev, static_cast<void*>(stream)}];
-  if (!w.side) {
-    if (pa::capturing(stream))
-      return set_error(PA_ERR_ALLOC, "the shared-prefix path's second stream is made at its "
-                       "first call on a stream, which is not done during graph capture: make "
-                       "one call on the stream before capturing");
-    hipStream_t sd = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
-    hipError_t e = hipStreamCreateWithFlags(&sd, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      if (j) (void)hipEventDestroy(j);
-      if (f) (void)hipEventDestroy(f);
-      if (sd) (void)hipStreamDestroy(sd);
-      return set_error(PA_ERR_LAUNCH, "second stream: %s", hipGetErrorString(e));
-    }
-    w.side = sd;
-    w.fork = f;
-    w.join = j;
-  }
-  *side = w.side;
-  *fork = w.fork;
-  *join = w.join;
   return PA_OK;
 }
 
@@ -401,9 +362,9 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
 
   // Prefix step: the S query rows of every KV head against the prefix keys,
   // one pseudo-sequence of S rows and prefix_len keys read through row 0 of
-  // the table, split into key chunks so that every CU gets a workgroup.  It
-  // runs on a second stream, concurrently with the suffix step (the decode
-  // kernel on each sequence's own keys); a third kernel joins the two.
+  // the table, split into key chunks.  It runs in the same kernel as the
+  // suffix step (the decode kernel on each sequence's own keys), as
+  // workgroups of their own; a second kernel joins the two.
   pa::PrefillPlan pp;
   pp.dtype = plan.dtype;
   pp.out_dtype = PA_F32;
@@ -419,8 +380,8 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   pp.pool = plan.pool;
   pp.max_query_len = plan.S;
   pp.causal = 0;
-  // Workgroups of four waves: the S rows are few, and smaller workgroups
-  // spread them over more CUs.
+  // Workgroups of four waves, like the decode workgroups they share compute
+  // units with.
   const int hg = plan.G > 4 ? 4 : plan.G;
   pp.row_waves = pa::kPrefixStepWaves / hg;
   const int step_rows = pa::kPrefillWaveRows * pp.row_waves;
@@ -437,7 +398,13 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   pp.fixed_n = prefix_len;
   const int ptiles = (prefix_len + 63) / 64;
   const int base = pp.q_tiles * plan.Hkv;
-  int chunks = std::max(1, std::min({ptiles, (256 + base - 1) / base, pa::kMaxPrefixChunks}));
+  // Key chunks: enough for about 128 prefill workgroups (one per two CUs;
+  // each CU also holds a decode workgroup), at most kMaxPrefixChunks.  More
+  // chunks finish the prefix sooner but write more partial results, which
+  // the join reads back: with 256 sequences and 8 KV heads one chunk (128
+  // workgroups) measured 123 us per call, two chunks 127 us.
+  const int chunks =
+      std::max(1, std::min({ptiles, (128 + base - 1) / base, pa::kMaxPrefixChunks}));
   pp.chunk_tiles = (ptiles + chunks - 1) / chunks;
   pp.n_chunks = (ptiles + pp.chunk_tiles - 1) / pp.chunk_tiles;
   pp.part_rows = plan.S;
@@ -457,10 +424,6 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   void* ws = nullptr;
   st = acquire_workspace(&plan, stream, &ws);
-  if (st) return st;
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  st = acquire_side(stream, &side, &fork, &join);
   if (st) return st;
   uint8_t* parts = static_cast<uint8_t*>(ws) + plan.counter_bytes;
   pp.part_o = reinterpret_cast<float*>(parts + chunk_off);
@@ -482,15 +445,6 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   jp.o_ss = plan.o_ss;
   jp.o_sh = plan.o_sh;
 
-  // Fork: the prefix step waits for the work queued on `stream` so far (the
-  // previous call's join kernel, which reads the same chunk region).
-  hipError_t e = hipEventRecord(fork, stream);
-  if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
-  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "fork: %s", hipGetErrorString(e));
-  e = pa::launch_prefill(pp, side);
-  if (e == hipSuccess) e = hipEventRecord(join, side);
-  if (e != hipSuccess)
-    return set_error(PA_ERR_LAUNCH, "shared-prefix launch: %s", hipGetErrorString(e));
   // Suffix step: keys [prefix_len, n_s) of every unit, its result as an f32
   // state (normalised output and natural-log log-sum-exp) in the workspace.
   plan.key_begin = prefix_len;
@@ -500,12 +454,9 @@ int pa_decode_shared_prefix(const pa_tensor* q, const pa_tensor* k_pool,
   plan.o_sh = plan.D;
   plan.lse = suf_lse;
   plan.lse_ss = plan.H;
-  e = pa::launch_decode(plan, ws, stream);
-  // Join: always wait for the prefix step, so that `stream` never runs
-  // ahead of work that uses its workspace.
-  const hipError_t ej = hipStreamWaitEvent(stream, join, 0);
-  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
-  if (ej != hipSuccess) return set_error(PA_ERR_LAUNCH, "join: %s", hipGetErrorString(ej));
+  hipError_t e = pa::launch_shared_prefix(plan, ws, pp, stream);
+  if (e != hipSuccess)
+    return set_error(PA_ERR_LAUNCH, "shared-prefix launch: %s", hipGetErrorString(e));
   e = pa::launch_prefix_join(jp, stream);
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "join launch: %s", hipGetErrorString(e));
   return PA_OK;
@@ -523,14 +474,6 @@ int pa_workspace_release(void* stream_ptr) {
   for (void* p : it->second.retired) {
     const hipError_t e2 = hipFreeAsync(p, stream);
     if (e == hipSuccess) e = e2;
-  }
-  if (it->second.side) {
-    // Every use of the second stream is joined back into `stream` before
-    // the frees above; wait for it before destroying it.
-    (void)hipStreamSynchronize(it->second.side);
-    (void)hipEventDestroy(it->second.fork);
-    (void)hipEventDestroy(it->second.join);
-    (void)hipStreamDestroy(it->second.side);
   }
   g_ws.erase(it);
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, "hipFreeAsync: %s", hipGetErrorString(e));

@@ -24,6 +24,11 @@ int decode_worker_count(int dtype, int D, int G);
 
 hipError_t launch_prefill(const PrefillPlan& plan, hipStream_t stream);
 
+// pa_decode_shared_prefix's prefix step (`pre`, prefill in key-chunk mode)
+// and suffix step (`dec`, with workspace `workspace`) as one kernel.
+hipError_t launch_shared_prefix(const DecodePlan& dec, void* workspace, const PrefillPlan& pre,
+                                hipStream_t stream);
+
 // Joins partial attention states (pa_merge_states).
 hipError_t launch_merge(const MergePlan& plan, hipStream_t stream);
 
