@@ -28,7 +28,8 @@ The same line carries:
   pool layout the library reads), the prefix-shared decode sweep
   (B = 16/32/64/128), the causal prefill (8 prompts of 512..4096 tokens,
   bf16; TFLOP/s against the bf16 MFMA peak, and against the peak at the
-  shader clock measured while it runs) and, as context for the HBM
+  shader clock measured while it runs), the same prompts with group sizes
+  1, 2 and 8 (kernel time only) and, as context for the HBM
   fractions, the rate of a plain 1 GiB device copy.
 """
 
@@ -74,7 +75,8 @@ def parse():
                          "check of the FETCH_SIZE scale factor (no GPU needed)")
     ap.add_argument("--only", default="",
                     help="comma list of workloads to run (for profiling): "
-                         "gqa,long,gqa-hm,long-hm,share,prefix,prefill,copy; prefix16 runs "
+                         "gqa,long,gqa-hm,long-hm,share,prefix,prefill,prefill-g,copy; "
+                         "prefill-g: the prefill prompts with 32, 16 and 4 KV heads; prefix16 runs "
                          "the prefix-shared workload at B = 16 only; -hm: pools head-major "
                          "within blocks; share: one eighth of the long context and the "
                          "merge of eight partial states")
@@ -83,13 +85,16 @@ def parse():
 
 # Headers every kernel source includes; a change in any of them can change
 # the compiled kernels, so they enter every kernel's source hash.
-SHARED_HEADERS = ("device_common.h", "kernels.h", "launch.h", "plan.h", "decode_kernel.h",
-                  "prefill_kernel.h")
+SHARED_HEADERS = ("device_common.h", "kernels.h", "launch.h", "plan.h")
+# The device code each kernel file compiles.
+KERNEL_FILES = {"decode.hip": ("decode.hip", "decode_kernel.h"),
+                "prefill.hip": ("prefill.hip", "prefill_kernel.h"),
+                "shared_prefix.hip": ("shared_prefix.hip", "decode_kernel.h", "prefill_kernel.h")}
 
 
-def source_hash(*names):
+def source_hash(kernel_file):
     h = hashlib.sha256()
-    for n in (*names, *SHARED_HEADERS):
+    for n in (*KERNEL_FILES[kernel_file], *SHARED_HEADERS):
         with open(os.path.join(ROOT, "paged_kv_cache_decode_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -685,6 +690,34 @@ def main():
                               f"{wall:.1f} s"}
             extra["causal-bf16-prefill"] = entry
             del d, call
+        # ------- the same prompts with other group sizes (G = 1, 2, 8) -------
+        if want("prefill-g"):
+            for hkv in (32, 16, 4):
+                case = W.causal_bf16_prefill(num_kv_heads=hkv)
+                flops = W.prefill_flops(case)
+                d = binding.upload_case(case)
+                out = torch.empty(case.q.shape, dtype=torch.bfloat16, device="cuda")
+                call = binding.PreparedPrefill(d["q"], d["k_pool"], d["v_pool"],
+                                               d["block_table"], d["context_lens"],
+                                               d["query_start_loc"], case.max_query_len,
+                                               case.scale, True, out)
+                for _ in range(3):
+                    call()
+                torch.cuda.synchronize()
+                binding.profiler_reset()
+                binding.profiler_enable(True)
+                Timer(torch).run(lambda i: call(), max(10, a.steps // 2))
+                binding.profiler_enable(False)
+                k_ms, _ = kernel_avg_ms(binding, "prefill")
+                k_spread = kernel_spread(binding, "prefill")
+                binding.profiler_reset()
+                G = 32 // hkv
+                extra[f"causal-bf16-prefill-G{G}"] = {
+                    "kv_heads": hkv, "kernel_TFLOP/s": round(flops / (k_ms * 1e-3) / 1e12, 1),
+                    "frac_of_bf16_mfma_peak": round(flops / (k_ms * 1e-3) / 1e12 /
+                                                    BF16_PEAK_TFLOPS, 4),
+                    "kernel_us": k_spread, "flops": flops}
+                del d, call, case
     if not a.headline_only and (not only or "copy" in only):
         gbs = copy_bandwidth(torch)
         extra["device_copy"] = {

@@ -284,11 +284,12 @@ def long_bf16_decode(num_seqs=4, context=100_000):
                             lens=[context] * num_seqs)
 
 
-def causal_bf16_prefill():
+def causal_bf16_prefill(num_kv_heads=8):
     """8 prompts, lengths uniform in [512, 4096], 32/8 heads, d=128, B=16,
-    causal, bfloat16; the prompts' own K/V are in the pool."""
-    return make_prefill_case(1004, 8, 32, 8, 128, 16, "bf16", len_range=(512, 4096),
-                             causal=True)
+    causal, bfloat16; the prompts' own K/V are in the pool.  Other KV head
+    counts give the same prompts with other group sizes."""
+    return make_prefill_case(1004, 8, 32, num_kv_heads, 128, 16, "bf16",
+                             len_range=(512, 4096), causal=True)
 
 
 def prefix_shared_bf16_decode(block_size):
