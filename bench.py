@@ -112,7 +112,10 @@ def load_traffic(kernel, workload, src_hash, bytes_per_launch):
     return {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
             "ratio_to_algorithmic": round((rec["fetch_bytes"] + rec["write_bytes"]) /
                                           bytes_per_launch, 4),
-            "scale_factor": rec.get("scale_factor"), "source": os.path.basename(path)}
+            "scale_factor": rec.get("scale_factor"),
+            "request_count_cross_check": (rec["rdreq_cross_check"]["over_scaled_fetch_bytes"]
+                                          if "rdreq_cross_check" in rec else None),
+            "source": os.path.basename(path)}
 
 
 # Kernel record name -> (substring of its demangled symbol, source).  The
