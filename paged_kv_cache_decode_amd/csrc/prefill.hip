@@ -12,7 +12,7 @@ namespace {
 template <class T, int HG, int RW>
 __global__ __launch_bounds__(64 * HG * RW)
 __attribute__((amdgpu_waves_per_eu(HG * RW == 16 ? 4 : 2))) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kPrefillLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[PrefillLds<HG, RW>::kBytes];
   prefill_body<T, HG, RW>(a, blockIdx.x, lds);
 }
 

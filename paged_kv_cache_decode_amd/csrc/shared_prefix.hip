@@ -31,7 +31,8 @@ struct SharedPrefixShape {
   static constexpr int kRW = kPrefixStepWaves / kHG;     // 16-row waves per head
   static constexpr bool kKRows = G <= 4;                 // decode reads K as whole rows
   static constexpr int kDecLds = DecodeLds<T, 128, G, kKRows>::kBytes;
-  static constexpr int kLds = kPrefillLdsBytes > kDecLds ? kPrefillLdsBytes : kDecLds;
+  static constexpr int kPreLds = PrefillLds<kHG, kRW>::kBytes;
+  static constexpr int kLds = kPreLds > kDecLds ? kPreLds : kDecLds;
   static_assert(kHG * kRW == kDecodeWaves, "both kinds of workgroup have four waves");
 };
 
@@ -41,8 +42,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void shared_prefix_kernel(DecodeArgs da,
                                                                   int dec_groups) {
   using Shape = SharedPrefixShape<T, G>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[Shape::kLds];
-  if ((int)blockIdx.x < dec_groups)
+  if ((int)blockIdx.x < dec_groups) {
     decode_body<T, 128, G, Shape::kKRows>(da, blockIdx.x, dec_groups, lds);
+  }
   else
     prefill_body<T, Shape::kHG, Shape::kRW>(pa, (int64_t)blockIdx.x - dec_groups, lds);
 }
