@@ -93,10 +93,16 @@ KERNEL_FILES = {"decode.hip": ("decode.hip", "decode_kernel.h"),
 
 
 def source_hash(kernel_file):
+    """Hash of the code a kernel file compiles, comments and blank space
+    left out (a comment edit does not change the kernel)."""
+    import re
     h = hashlib.sha256()
     for n in (*KERNEL_FILES[kernel_file], *SHARED_HEADERS):
-        with open(os.path.join(ROOT, "paged_kv_cache_decode_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_decode_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

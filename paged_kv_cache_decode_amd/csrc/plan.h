@@ -107,8 +107,8 @@ struct PrefillPlan {
   int64_t o_st = 0, o_sh = 0;
   float scale = 0.f;
   // Shared-prefix attention (decode with a common prefix): one sequence given
-  // by value and key chunks writing partial results, merged by the decode
-  // kernel; see prefill.hip.
+  // by value and key chunks writing partial results, merged by the join
+  // kernel; see prefill_kernel.h and shared_prefix.hip.
   int fixed_L = -1, fixed_n = 0;
   int n_chunks = 1, chunk_tiles = 1 << 30;
   int64_t part_rows = 0;
@@ -116,7 +116,7 @@ struct PrefillPlan {
   float* part_lse = nullptr;
 };
 
-// Most key chunks the shared-prefix step splits its keys into (the decode
+// Most key chunks the shared-prefix step splits its keys into (the join
 // kernel merges them keeping every chunk's part in registers).
 constexpr int kMaxPrefixChunks = 4;
 
