@@ -102,6 +102,9 @@ struct PrefillArgs {
   int64_t part_rows;
   float* part_o;
   float* part_lse;
+  // Packed prompts whose head groups split evenly over the 8 XCDs, at
+  // most 64 (group, sequence) pairs per XCD: work items from packed_item.
+  int packed_order;
 };
 
 template <class T>
@@ -165,6 +168,53 @@ __device__ __forceinline__ float row4_sum(float x) {
   return x + xor32(x);
 }
 
+// Work item of packed-prompt workgroup `bid` (its hardware number): head
+// group `grp`, sequence `s`, query tile `qt` of kRowsWG rows; false when the
+// workgroup has none.  The (group, sequence) pairs are cut into 8 equal
+// contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so that
+// all query tiles of a pair share its K/V in one L2; with the number of
+// groups a multiple of 8 every range holds whole groups and the same work.
+// Within its range an XCD takes the pairs in order of decreasing context
+// length (ties by position) and each pair's query tiles from the last,
+// which visits the most keys: the longest tiles start first, the short
+// ones of the short sequences fill the end, a pair's tiles run together
+// while its K/V is in L2, and the workgroups with no tile come after every
+// real one in dispatch order.  Lane i of every wave holds pair i of the
+// range (at most 64).
+template <int kRowsWG>
+__device__ __forceinline__ bool packed_item(const PrefillArgs& a, int64_t bid, int& grp, int& s,
+                                            int& qt) {
+  const int lane = threadIdx.x & 63;
+  const int n_pairs = a.Hkv * a.kv_div * a.S;
+  const int ppx = (n_pairs + 7) >> 3;
+  const int p_lo = min(n_pairs, (int)(bid & 7) * ppx);
+  const int np = min(n_pairs - p_lo, ppx);
+  const int j = (int)(bid >> 3);
+  int T = 0, n = 0;
+  if (lane < np) {
+    const int ss = (p_lo + lane) % a.S;
+    const int q0 = a.qsl[ss];
+    const int L = a.qsl[ss + 1] - q0;
+    n = a.cl[ss];
+    T = L > 0 ? min(a.q_tiles, (L + kRowsWG - 1) / kRowsWG) : 0;
+  }
+  // Tiles of the pairs ahead of this lane's pair in the order.
+  int start = 0;
+  for (int p = 0; p < np; ++p) {
+    const int np_ = __builtin_amdgcn_readlane(n, p);
+    const int tp = __builtin_amdgcn_readlane(T, p);
+    start += (np_ > n || (np_ == n && p < lane)) ? tp : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < np && start <= j && j < start + T);
+  if (hit == 0) return false;
+  const int src = __builtin_ctzll(hit);
+  const int pair = p_lo + src;
+  grp = pair / a.S;
+  s = pair % a.S;
+  qt = __builtin_amdgcn_readlane(T, src) - 1 - (j - __builtin_amdgcn_readlane(start, src));
+  return true;
+}
+
 // V^T in LDS: row d holds the tile's 64 keys as fp16, in an order that puts
 // the 8 keys one lane feeds to a P.V MFMA next to each other.  The lane
 // (row r16, group g4) of 32-key step s2 holds, as the MFMA's B operand, the
@@ -212,17 +262,23 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int64_t bid, 
   auto k_lds = reinterpret_cast<uint8_t (*)[kKBytes]>(lds);
   auto vt_lds = reinterpret_cast<uint8_t (*)[kVBytes]>(lds + 2 * kKBytes);
 
-  // XCD-aware order: hardware workgroup b runs on XCD b % 8; give each XCD
-  // a contiguous slice of the logical order (g, s, query tile descending).
-  const int64_t logical_c = (bid & 7) * a.wg_per_xcd + (bid >> 3);
-  if (logical_c >= a.n_wg) return;
-  const int chunk = (int)(logical_c % a.n_chunks);
-  const int64_t logical = logical_c / a.n_chunks;
-  const int per_g = a.S * a.q_tiles;
-  const int g = (int)(logical / per_g);
-  const int rem = (int)(logical % per_g);
-  const int s = rem / a.q_tiles;
-  const int qt = a.q_tiles - 1 - rem % a.q_tiles;
+  int g = 0, s = 0, qt = 0, chunk = 0;
+  if (a.packed_order) {
+    if (!packed_item<kRows>(a, bid, g, s, qt)) return;
+  } else {
+    // XCD-aware order: hardware workgroup b runs on XCD b % 8; each XCD
+    // takes a contiguous slice of the logical order (g, s, query tile
+    // descending, key chunk).
+    const int64_t logical_c = (bid & 7) * a.wg_per_xcd + (bid >> 3);
+    if (logical_c >= a.n_wg) return;
+    chunk = (int)(logical_c % a.n_chunks);
+    const int64_t logical = logical_c / a.n_chunks;
+    const int per_g = a.S * a.q_tiles;
+    g = (int)(logical / per_g);
+    const int rem = (int)(logical % per_g);
+    s = rem / a.q_tiles;
+    qt = a.q_tiles - 1 - rem % a.q_tiles;
+  }
 
   const const_i32_ptr qsl = as_const(a.qsl);
   const int q0 = a.fixed_L >= 0 ? 0 : qsl[s];
@@ -562,6 +618,10 @@ inline PrefillArgs prefill_args(const PrefillPlan& pl) {
   a.kv_div = pl.G > 4 ? pl.G / 4 : 1;
   a.n_wg = (int64_t)pl.q_tiles * pl.Hkv * a.kv_div * pl.S * pl.n_chunks;
   a.wg_per_xcd = (a.n_wg + 7) / 8;
+  const int64_t groups = (int64_t)pl.Hkv * a.kv_div;
+  const int64_t ppx = (groups * pl.S + 7) / 8;
+  a.packed_order = pl.fixed_L < 0 && pl.n_chunks == 1 && groups % 8 == 0 && ppx <= 64;
+  if (a.packed_order) a.wg_per_xcd = ppx * pl.q_tiles;
   return a;
 }
 
