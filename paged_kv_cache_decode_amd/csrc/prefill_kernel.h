@@ -169,8 +169,8 @@ __device__ __forceinline__ float row4_sum(float x) {
 }
 
 // Work item of packed-prompt workgroup `bid` (its hardware number): head
-// group `grp`, sequence `s`, query tile `qt` of kRowsWG rows; false when the
-// workgroup has none.  The (group, sequence) pairs are cut into 8 equal
+// group `grp`, sequence `s` (query rows from q0, L of them, n keys), query
+// tile `qt` of kRowsWG rows; false when the workgroup has none.  The (group, sequence) pairs are cut into 8 equal
 // contiguous ranges, one per XCD (workgroup b runs on XCD b % 8), so that
 // all query tiles of a pair share its K/V in one L2; with the number of
 // groups a multiple of 8 every range holds whole groups and the same work.
@@ -183,27 +183,27 @@ __device__ __forceinline__ float row4_sum(float x) {
 // range (at most 64).
 template <int kRowsWG>
 __device__ __forceinline__ bool packed_item(const PrefillArgs& a, int64_t bid, int& grp, int& s,
-                                            int& qt) {
+                                            int& qt, int& q0, int& L, int& n) {
   const int lane = threadIdx.x & 63;
   const int n_pairs = a.Hkv * a.kv_div * a.S;
   const int ppx = (n_pairs + 7) >> 3;
   const int p_lo = min(n_pairs, (int)(bid & 7) * ppx);
   const int np = min(n_pairs - p_lo, ppx);
   const int j = (int)(bid >> 3);
-  int T = 0, n = 0;
+  int T = 0, lq0 = 0, lL = 0, ln = 0;
   if (lane < np) {
     const int ss = (p_lo + lane) % a.S;
-    const int q0 = a.qsl[ss];
-    const int L = a.qsl[ss + 1] - q0;
-    n = a.cl[ss];
-    T = L > 0 ? min(a.q_tiles, (L + kRowsWG - 1) / kRowsWG) : 0;
+    lq0 = a.qsl[ss];
+    lL = a.qsl[ss + 1] - lq0;
+    ln = a.cl[ss];
+    T = lL > 0 ? min(a.q_tiles, (lL + kRowsWG - 1) / kRowsWG) : 0;
   }
   // Tiles of the pairs ahead of this lane's pair in the order.
   int start = 0;
   for (int p = 0; p < np; ++p) {
-    const int np_ = __builtin_amdgcn_readlane(n, p);
+    const int np_ = __builtin_amdgcn_readlane(ln, p);
     const int tp = __builtin_amdgcn_readlane(T, p);
-    start += (np_ > n || (np_ == n && p < lane)) ? tp : 0;
+    start += (np_ > ln || (np_ == ln && p < lane)) ? tp : 0;
   }
   const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < np && start <= j && j < start + T);
   if (hit == 0) return false;
@@ -212,6 +212,9 @@ __device__ __forceinline__ bool packed_item(const PrefillArgs& a, int64_t bid, i
   grp = pair / a.S;
   s = pair % a.S;
   qt = __builtin_amdgcn_readlane(T, src) - 1 - (j - __builtin_amdgcn_readlane(start, src));
+  q0 = __builtin_amdgcn_readlane(lq0, src);
+  L = __builtin_amdgcn_readlane(lL, src);
+  n = __builtin_amdgcn_readlane(ln, src);
   return true;
 }
 
@@ -262,9 +265,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int64_t bid, 
   auto k_lds = reinterpret_cast<uint8_t (*)[kKBytes]>(lds);
   auto vt_lds = reinterpret_cast<uint8_t (*)[kVBytes]>(lds + 2 * kKBytes);
 
-  int g = 0, s = 0, qt = 0, chunk = 0;
+  int g = 0, s = 0, qt = 0, chunk = 0, q0 = 0, L = 0, n = 0;
   if (a.packed_order) {
-    if (!packed_item<kRows>(a, bid, g, s, qt)) return;
+    if (!packed_item<kRows>(a, bid, g, s, qt, q0, L, n)) return;
   } else {
     // XCD-aware order: hardware workgroup b runs on XCD b % 8; each XCD
     // takes a contiguous slice of the logical order (g, s, query tile
@@ -278,12 +281,11 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int64_t bid, 
     const int rem = (int)(logical % per_g);
     s = rem / a.q_tiles;
     qt = a.q_tiles - 1 - rem % a.q_tiles;
+    const const_i32_ptr qsl = as_const(a.qsl);
+    q0 = a.fixed_L >= 0 ? 0 : qsl[s];
+    L = a.fixed_L >= 0 ? a.fixed_L : qsl[s + 1] - q0;
+    n = a.fixed_L >= 0 ? a.fixed_n : as_const(a.cl)[s];
   }
-
-  const const_i32_ptr qsl = as_const(a.qsl);
-  const int q0 = a.fixed_L >= 0 ? 0 : qsl[s];
-  const int L = a.fixed_L >= 0 ? a.fixed_L : qsl[s + 1] - q0;
-  const int n = a.fixed_L >= 0 ? a.fixed_n : as_const(a.cl)[s];
   if (qt * kRows >= L) return;
 
   const int tid = threadIdx.x;
@@ -487,8 +489,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int64_t bid, 
   // This workgroup's tiles: [kt0, kt1) (all of [0, ntk) without chunking).
   const int kt0 = min(ntk, chunk * a.chunk_tiles);
   const int kt1 = min(ntk, kt0 + a.chunk_tiles);
-  // One barrier per tile: while the waves compute on tile kt, tile kt + 1 is
-  // written to the free buffers and tile kt + 2 is fetched.
+  // One barrier per tile: after computing on tile kt a wave writes its part
+  // of tile kt + 1 (fetched during step kt - 1) to the free buffers and
+  // fetches tile kt + 2, which then has all of step kt + 1 to arrive.
   u32x4_t kreg[kKPer];
   u32x4_t vreg[kVPer][2];
   auto load_tile = [&](int kt) {
@@ -522,18 +525,19 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int64_t bid, 
   const bool delayed = PrefillLds<HG, RW>::kDelayPV && ((w >> 2) & 1);
   for (int kt = kt0; kt < kt1; ++kt) {
     // Tile kt is in K buffer kt & 1 and V^T buffer kt % kVBufs; the buffers
-    // of tile kt + 1 are free (nobody reads tile kt - 1's K any more, nor,
-    // with three V^T buffers, tile kt - 2's V^T).
+    // of tile kt + 1 are free (tile kt - 1's K was last read in step
+    // kt - 1, tile kt - 2's V^T in step kt - 1 at the latest; with two V^T
+    // buffers, and no delayed P.V, tile kt - 1's V^T in step kt - 1).
     __syncthreads();
-    if (kt + 1 < kt1) {
-      store_tile(kt + 1);
-      if (kt + 2 < kt1) load_tile(kt + 2);
-    }
     if (delayed && kt > kt0 && kt - 1 <= last) pv_step(kt - 1);
     if (kt <= last) {
       qk_step(kt);
       softmax_tile(kt);
       if (!delayed) pv_step(kt);
+    }
+    if (kt + 1 < kt1) {
+      store_tile(kt + 1);
+      if (kt + 2 < kt1) load_tile(kt + 2);
     }
   }
   if (delayed && kt0 < kt1 && kt1 - 1 <= last) pv_step(kt1 - 1);
