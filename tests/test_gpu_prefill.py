@@ -101,6 +101,41 @@ def test_prefill_many_prompts(pa):
     assert_close_f32_out(sel, ref, "bf16", "90 prompts")
 
 
+@pytest.mark.parametrize("G,S", [(4, 64), (4, 65), (2, 24), (1, 8), (8, 40)])
+def test_prefill_work_order(pa, G, S):
+    """32 query heads in head groups that split evenly over the 8 XCDs: the
+    kernel orders each XCD's query tiles itself (sequences by decreasing
+    context length, ties by position, tiles from the last).  64 (group,
+    sequence) pairs per XCD is the largest such case (G = 4, S = 64); S = 65
+    takes the plain order.  Prompts of 0 and 1 query rows, prompts that
+    continue a longer context and equal context lengths; every 7th row and
+    each prompt's first and last rows, at a random head each, so every query
+    tile is checked."""
+    rng = np.random.default_rng(440 + 10 * G + S)
+    lens = [int(x) for x in rng.integers(1, 300, size=S)]
+    for i in range(0, S, 9):
+        lens[i] = lens[(i + 4) % S]                  # ties in context length
+    qlens = []
+    for i, n in enumerate(lens):
+        r = rng.random()
+        qlens.append(0 if i % 11 == 3 else 1 if i % 13 == 5 else
+                     n if r < 0.7 else int(rng.integers(1, n + 1)))
+    c = W.make_prefill_case(450 + G, S, 32, 32 // G, 128, 16, "bf16", lens=lens,
+                            query_lens=qlens, causal=True)
+    got = out_to_f64(run_prefill(pa, c))
+    qsl = c.query_start_loc
+    rows = set()
+    for s in range(S):
+        if qsl[s + 1] > qsl[s]:
+            rows.update({int(qsl[s]), int(qsl[s + 1] - 1)})
+    rows.update(range(0, int(qsl[-1]), 7))
+    rows = [(t, int(rng.integers(0, 32))) for t in sorted(rows)]
+    ref, _ = oracle.prefill_rows(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, qsl,
+                                 c.scale, True, c.dtype, rows)
+    sel = np.stack([got[t, h] for t, h in rows])
+    assert_close_f32_out(sel, ref, "bf16", f"work order G={G} S={S}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_write_kv_bit_exact(pa, dtype):
     rng = np.random.default_rng(5)
