@@ -43,9 +43,12 @@
 // masking code.
 //
 // Workgroups are ordered so that each XCD (8 per MI355X, fed round-robin)
-// works through a contiguous slice of (KV head, sequence, query tile), with
-// a sequence's query tiles longest-first; the tiles running together on an
-// XCD then share the same K/V in its L2.
+// works through whole (head group, sequence) pairs, so that the tiles
+// running together on an XCD share the same K/V in its L2.  Packed prompts
+// (packed_item) take the pairs in order of decreasing context length and
+// each pair's query tiles from the last, the longest, with no empty
+// workgroup ahead of a real one; other shapes take a contiguous slice of
+// (head group, sequence, query tile descending) per XCD.
 #pragma once
 
 #include <type_traits>
