@@ -328,8 +328,29 @@ def kernel_spread(binding, name):
     return spread_us(binding.profiler_samples(name))
 
 
+def warm_up(torch, fn, steps, min_seconds):
+    """Untimed calls: `steps` of them, then more (in groups of 10) until at
+    least `min_seconds` have passed, so that the GPU's clocks have settled
+    when a measurement starts after idle time (uploads, other workloads)."""
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    i = steps
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(10):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
+# Time-based warm-up of the `extra` entries (the headline keeps exactly the
+# --warmup steps of the command line).
+EXTRA_WARM_S = 0.1
+
+
 def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
-                      prefix_len=None, head_major=False):
+                      prefix_len=None, head_major=False, warm_seconds=0.0):
     """Time pa_decode (or pa_decode_shared_prefix with ``prefix_len``) on a
     case, rotating over `copies` device copies of the pools (token-major, or
     head-major within blocks).  Returns a dict of timings."""
@@ -342,8 +363,7 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
                                devs[0]["block_table"], devs[0]["context_lens"], out)
     step = lambda i: calls[i % copies]()  # noqa: E731
     timer = Timer(torch)
-    for i in range(warmup):
-        step(i)
+    warm_up(torch, step, warmup, warm_seconds)
     sec = timer.run(step, steps)
     # Second pass with the library's per-kernel event timer on.
     binding.profiler_reset()
@@ -365,7 +385,7 @@ def bench_decode_case(torch, binding, case, steps, warmup, copies, out_dtype,
                 step_spread=step_spread)
 
 
-def bench_long_share(torch, binding, W, steps):
+def bench_long_share(torch, binding, W, steps, warmup):
     """The long-context workload split eight ways by contiguous block ranges
     (the split across GPUs that pa_decode_lse + pa_merge_states serve): one
     range's pa_decode_lse and the merge of eight such partial states, timed
@@ -387,10 +407,10 @@ def bench_long_share(torch, binding, W, steps):
     merged = torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda")
     call = lambda: binding.decode_lse(d["q"], d["k_pool"], d["v_pool"], d["block_table"],  # noqa
                                       d["context_lens"], case.scale, out=out, lse=lse)
-    for _ in range(3):
+    def both(i):
         call()
         binding.merge_states(parts, part_lse, out=merged, want_lse=False)
-    torch.cuda.synchronize()
+    warm_up(torch, both, warmup, EXTRA_WARM_S)
     binding.profiler_reset()
     binding.profiler_enable(True)
     for _ in range(steps):
@@ -538,8 +558,8 @@ def main():
         if want("long"):
             case = W.long_bf16_decode()
             nbytes = W.decode_bytes(case, out_bytes_per_elem=2)
-            r = bench_decode_case(torch, binding, case, max(10, a.steps // 2), 3, 1,
-                                  torch.bfloat16)
+            r = bench_decode_case(torch, binding, case, max(10, a.steps // 2), a.warmup, 1,
+                                  torch.bfloat16, warm_seconds=EXTRA_WARM_S)
             lgbs = nbytes / (r["part_ms"] * 1e-3) / 1e9
             extra["long-bf16-decode"] = {
                 "GB/s": round(nbytes / r["sec"] / 1e9, 1),
@@ -570,7 +590,8 @@ def main():
                 continue
             case = make()
             nbytes = W.decode_bytes(case, out_bytes_per_elem=2)
-            rh = bench_decode_case(torch, binding, case, steps, 3, copies, odt,
+            rh = bench_decode_case(torch, binding, case, steps, a.warmup, copies, odt,
+                                   warm_seconds=EXTRA_WARM_S,
                                    head_major=True)
             extra[name] = {
                 "GB/s": round(nbytes / rh["sec"] / 1e9, 1),
@@ -586,7 +607,8 @@ def main():
         # ---- one GPU's share of the long context split eight ways ----------
         if want("share"):
             extra["long-bf16-decode-8way-share"] = bench_long_share(torch, binding, W,
-                                                                    max(10, a.steps // 2))
+                                                                    max(10, a.steps // 2),
+                                                                    a.warmup)
         # ---------------- prefix-shared decode sweep ---------------------
         if want("prefix") or want("prefix16"):
             for B in ((16, 32, 64, 128) if want("prefix") else (16,)):
@@ -594,10 +616,11 @@ def main():
                 logical = W.decode_bytes(case, out_bytes_per_elem=2)
                 unique = (case.meta["unique_tokens"] * 8 * 128 * 2 * 2 +
                           logical - int(case.context_lens.sum()) * 8 * 128 * 2 * 2)
-                r = bench_decode_case(torch, binding, case, max(10, a.steps // 2), 3, 3,
-                                      torch.bfloat16)
-                rc = bench_decode_case(torch, binding, case, max(10, a.steps), 3, 3,
-                                       torch.bfloat16, prefix_len=case.meta["prefix_len"])
+                r = bench_decode_case(torch, binding, case, max(10, a.steps // 2), a.warmup, 3,
+                                      torch.bfloat16, warm_seconds=EXTRA_WARM_S)
+                rc = bench_decode_case(torch, binding, case, max(10, a.steps), a.warmup, 3,
+                                       torch.bfloat16, prefix_len=case.meta["prefix_len"],
+                                       warm_seconds=EXTRA_WARM_S)
                 med = rc["step_spread"]["median"] * 1e-6
                 extra[f"prefix-shared-bf16-decode-B{B}"] = {
                     "unique_GB/s": round(unique / r["sec"] / 1e9, 1),
@@ -633,8 +656,7 @@ def main():
                                            d["context_lens"], d["query_start_loc"],
                                            case.max_query_len, case.scale, True, out)
             timer = Timer(torch)
-            for _ in range(3):
-                call()
+            warm_up(torch, lambda i: call(), a.warmup, EXTRA_WARM_S)
             steps = max(10, a.steps // 2)
             sec = timer.run(lambda i: call(), steps)
             binding.profiler_reset()
@@ -713,9 +735,7 @@ def main():
                                                d["block_table"], d["context_lens"],
                                                d["query_start_loc"], case.max_query_len,
                                                case.scale, True, out)
-                for _ in range(3):
-                    call()
-                torch.cuda.synchronize()
+                warm_up(torch, lambda i: call(), a.warmup, EXTRA_WARM_S)
                 binding.profiler_reset()
                 binding.profiler_enable(True)
                 Timer(torch).run(lambda i: call(), max(10, a.steps // 2))
