@@ -5,6 +5,7 @@ import csv
 import json
 import os
 import sys
+import time
 
 import pytest
 
@@ -99,3 +100,28 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_warm_up_counts_and_time():
+    """Exactly `steps` calls without a time floor; with one, more calls in
+    groups of 10 until the floor has passed (each group synchronised)."""
+    class FakeCuda:
+        syncs = 0
+
+        @classmethod
+        def synchronize(cls):
+            cls.syncs += 1
+
+    class FakeTorch:
+        cuda = FakeCuda
+
+    calls = []
+    bench.warm_up(FakeTorch, calls.append, 7, 0.0)
+    assert calls == list(range(7)) and FakeCuda.syncs == 1
+    calls.clear()
+    FakeCuda.syncs = 0
+    t0 = time.perf_counter()
+    bench.warm_up(FakeTorch, lambda i: (calls.append(i), time.sleep(0.001)), 3, 0.05)
+    assert time.perf_counter() - t0 >= 0.05
+    assert calls == list(range(len(calls))) and len(calls) >= 13 and (len(calls) - 3) % 10 == 0
+    assert FakeCuda.syncs == 1 + (len(calls) - 3) // 10
