@@ -21,9 +21,10 @@
 //   exponentials interleave.  K/V tiles of 64 keys are gathered once per
 //   workgroup into LDS and feed all its waves.  Key tiles wholly above the
 //   diagonal are never loaded.  LDS is double buffered (V^T triple buffered
-//   in sixteen-wave workgroups): while the waves compute on one tile the
-//   next one is written to the free buffers from registers, and the tile
-//   after that is already being fetched, so there is one barrier per tile.
+//   in sixteen-wave workgroups): after computing on one tile a wave writes
+//   its part of the next one, fetched during the previous step, to the free
+//   buffers and fetches the tile after it, so there is one barrier per
+//   tile.
 //
 // Per 64-key tile a wave computes, on 16x16x32 MFMAs:
 //   S^T = K Q^T   (A = K from LDS, B = Q from registers; bf16/f16 inputs,
