@@ -551,6 +551,18 @@ def main():
                 "sample": f"the whole workload (64 sequences x 32 heads), {passes} pass(es), "
                           f"{sec:.2f} s per pass, fp64 numpy",
                 "host": host, "avg_busy_threads": round(busy, 2)}
+        if not a.headline_only:
+            # The same workload and step after the extra entries' time-based
+            # warm-up: the steady-state step rate, as context for `value`.
+            rs = bench_decode_case(torch, binding, case, a.steps, a.warmup, 3, torch.float16,
+                                   warm_seconds=EXTRA_WARM_S)
+            extra["gqa-f16-decode-steady"] = {
+                "GB/s": round(nbytes / rs["sec"] / 1e9, 1),
+                "frac_of_hbm_peak": round(nbytes / rs["sec"] / 1e9 / HBM_PEAK_GBS, 4),
+                "ms_per_step": round(rs["sec"] * 1e3, 4),
+                "step_us": rs["step_spread"],
+                "partition_kernel_us": rs["part_spread"],
+                "warm_up": f"{a.warmup} calls, then until {EXTRA_WARM_S} s had passed"}
         del case
 
     if not a.headline_only:
