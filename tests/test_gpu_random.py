@@ -73,12 +73,12 @@ def test_decode_random_configs(pa, monkeypatch, seed):
         assert_close_native_out(out_to_f64(nat), ref, dtype, what + " native out")
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(16))
 def test_prefill_random_configs(pa, seed):
     rng = np.random.default_rng(7000 + seed)
     dtype = str(rng.choice(["f16", "bf16"]))
     G = int(rng.choice([1, 2, 4, 8]))
-    Hkv = int(rng.choice([1, 2, 4]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
     B = int(rng.choice([16, 32, 64, 128]))
     S = int(rng.integers(1, 7))
     causal = bool(rng.integers(0, 2))
